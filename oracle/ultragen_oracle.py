@@ -1,0 +1,317 @@
+"""fp64 CPU oracle for UltraGen's composite-masked hierarchical local attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  The GPU library never calls it, and
+it shares no code, header or table with the library.
+
+Sources (cited by page title and section):
+  [KD1] "UltraGen: Efficient Ultra-High-Resolution Image Generation with
+        Hierarchical Local Attention", papernotes.org notes, 关键设计 1
+        (window-first local window attention): non-overlapping l x l windows,
+        l = 16, tokens regrouped window by window, adjacent-window interaction.
+  [KD2] same page, 关键设计 2 (scale-aligned low-resolution guidance): the LR
+        latent with rho = H/h, the coordinate map (m, n) -> (rho*m, rho*n), and
+        the attention-mask description (text <-> itself and HR; HR -> own and
+        adjacent windows, text and LR anchors; LR -> all LR).
+  [KD3] same page, 关键设计 3: the joint sequence [C_T; X; X_lr] and the joint
+        attention softmax(Q K^T (masked) / sqrt(d)) V.
+  [GS-B] "UltraGen ..." summary on gist.science (paper 2510.16325), section
+        2.B (Attention Masking): windows attend to themselves and adjacent
+        windows and to the scaled global guidance tokens; LR tokens attend
+        globally to each other.
+
+Everything is computed in float64, in RASTER order (text rows, then HR rows
+r*W + c, then LR rows m*w + n), and every mask decision is taken from 2D
+coordinates, never from a permutation.  Readings of points the pages leave
+open (all listed in the design doc's table of readings):
+  R1 windows and tokens inside a window are both ordered row-major;
+  R2 ragged grids use a ceil partition with partial edge windows and a compact
+     permutation (no padding);
+  R3 LR grid defaults to ceil(H/rho) x ceil(W/rho); LR position = (rho*m, rho*n);
+  R4 text tokens sit at position (0, 0), i.e. are not rotated;
+  R5 axial RoPE: first half of the head dims rotated by the row position, second
+     half by the column position, adjacent pairs (x[2k], x[2k+1]), frequency
+     omega_k = theta^(-2k/(D/2)), k = 0 .. D/4-1;
+  R6 the mask is additive -inf (masked keys excluded), scale 1/sqrt(D), one
+     softmax over the union of allowed keys;
+  R7 "adjacent" = Chebyshev window distance <= radius (radius 1 = 3x3 windows);
+  R8 HR queries see ALL LR tokens; LR queries see LR and text; text queries see
+     text and HR, not LR.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+TEXT, HR, LR = 0, 1, 2
+
+
+@dataclass(frozen=True)
+class Geometry:
+    """Token grid geometry of one attention layer ([KD1], [KD2], [KD3])."""
+    hr_h: int
+    hr_w: int
+    lr_h: int
+    lr_w: int
+    n_text: int
+    window: int
+    radius: int
+    rho: int
+
+    @property
+    def n_hr(self):
+        return self.hr_h * self.hr_w
+
+    @property
+    def n_lr(self):
+        return self.lr_h * self.lr_w
+
+    @property
+    def seq_len(self):
+        return self.n_text + self.n_hr + self.n_lr
+
+    @property
+    def grid(self):
+        """Windows per column / row of the HR grid: ceil partition (R2)."""
+        return (-(-self.hr_h // self.window), -(-self.hr_w // self.window))
+
+
+def geometry(hr_h, hr_w, n_text, window=16, radius=1, rho=4, lr_h=None, lr_w=None) -> Geometry:
+    """LR grid defaults to ceil(H/rho) x ceil(W/rho), since rho = H/h ([KD2], R3);
+    an explicit 0 means no LR tokens."""
+    if lr_h is None:
+        lr_h = -(-hr_h // rho)
+    if lr_w is None:
+        lr_w = -(-hr_w // rho)
+    return Geometry(hr_h, hr_w, lr_h, lr_w, n_text, window, radius, rho)
+
+
+def geometry_of(w) -> Geometry:
+    """Geometry of a workloads.Workload (duck-typed)."""
+    return geometry(w.hr_h, w.hr_w, w.n_text, w.window, w.radius, w.rho, w.lr_h, w.lr_w)
+
+
+def token_coords(g: Geometry):
+    """Per raster row: kind, RoPE position (row, col) and HR window (wy, wx).
+
+    HR token r*W + c sits at (r, c) in window (r // l, c // l) [KD1]; LR token
+    m*w + n sits at (rho*m, rho*n) [KD2]; text sits at (0, 0) (R4).  Window
+    coordinates of non-HR rows are -1.
+    """
+    L = g.seq_len
+    kind = np.empty(L, np.int64)
+    pr = np.zeros(L, np.int64)
+    pc = np.zeros(L, np.int64)
+    wy = np.full(L, -1, np.int64)
+    wx = np.full(L, -1, np.int64)
+    T, N = g.n_text, g.n_hr
+    kind[:T] = TEXT
+    kind[T:T + N] = HR
+    kind[T + N:] = LR
+    r, c = np.divmod(np.arange(N), g.hr_w)
+    pr[T:T + N], pc[T:T + N] = r, c
+    wy[T:T + N], wx[T:T + N] = r // g.window, c // g.window
+    m, n = np.divmod(np.arange(g.n_lr), g.lr_w)
+    pr[T + N:], pc[T + N:] = g.rho * m, g.rho * n
+    return kind, pr, pc, wy, wx
+
+
+# --------------------------------------------------------------------------
+# Window-first order and window adjacency, derived from coordinates
+# --------------------------------------------------------------------------
+
+def window_first_perm(hr_h: int, hr_w: int, window: int) -> np.ndarray:
+    """perm[j] = raster index of the j-th HR token in window-first order.
+
+    [KD1]: the token sequence is regrouped window by window so that each
+    window is one contiguous block.  Sort key (R1): window row, window column,
+    row inside the window, column inside the window.
+    """
+    r, c = np.divmod(np.arange(hr_h * hr_w), hr_w)
+    keys = (c % window, r % window, c // window, r // window)  # lexsort: last key is primary
+    return np.lexsort(keys).astype(np.int64)
+
+
+def window_offsets(hr_h: int, hr_w: int, window: int) -> np.ndarray:
+    """Start of each window (row-major window order) in window-first order."""
+    gy, gx = -(-hr_h // window), -(-hr_w // window)
+    sizes = []
+    for a in range(gy):
+        for b in range(gx):
+            hy = min(window, hr_h - a * window)
+            hx = min(window, hr_w - b * window)
+            sizes.append(hy * hx)
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+
+
+def neighbour_windows(hr_h: int, hr_w: int, window: int, radius: int):
+    """For each window (row-major), the windows within Chebyshev distance
+    `radius` (its own included), ascending by window index ([KD1] adjacent
+    windows, [GS-B], R7).  Returns (flat list, offsets)."""
+    gy, gx = -(-hr_h // window), -(-hr_w // window)
+    flat, off = [], [0]
+    for a in range(gy):
+        for b in range(gx):
+            for a2 in range(gy):
+                for b2 in range(gx):
+                    if max(abs(a - a2), abs(b - b2)) <= radius:
+                        flat.append(a2 * gx + b2)
+            off.append(len(flat))
+    return np.asarray(flat, np.int64), np.asarray(off, np.int64)
+
+
+# --------------------------------------------------------------------------
+# 2D axial RoPE ([KD1] RoPE range, [KD2] scaled LR positions; R4, R5)
+# --------------------------------------------------------------------------
+
+def rope_rotate(x: np.ndarray, pos_r: np.ndarray, pos_c: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate rows of x [n, D] (float64) at positions (pos_r, pos_c).
+
+    Dims [0, D/2) carry the row position, dims [D/2, D) the column position.
+    Inside each half, pair (2k, 2k+1) turns by angle pos * theta^(-2k/(D/2)):
+    (a, b) -> (a cos - b sin, a sin + b cos).
+    """
+    n, D = x.shape
+    assert D % 4 == 0
+    half = D // 2
+    k = np.arange(D // 4, dtype=np.float64)
+    omega = theta ** (-2.0 * k / half)
+    out = np.array(x, dtype=np.float64, copy=True)
+    for base, pos in ((0, pos_r), (half, pos_c)):
+        ang = np.asarray(pos, np.float64)[:, None] * omega[None, :]
+        cs, sn = np.cos(ang), np.sin(ang)
+        a = x[:, base + 0:base + half:2]
+        b = x[:, base + 1:base + half:2]
+        out[:, base + 0:base + half:2] = a * cs - b * sn
+        out[:, base + 1:base + half:2] = a * sn + b * cs
+    return out
+
+
+# --------------------------------------------------------------------------
+# The composite mask ([KD2], [GS-B], [KD3]; R6-R8)
+# --------------------------------------------------------------------------
+
+def allowed_keys_of(g: Geometry, coords, i: int) -> np.ndarray:
+    """Raster indices of the keys query row i may attend to."""
+    kind, _, _, wy, wx = coords
+    if kind[i] == TEXT:
+        ok = (kind == TEXT) | (kind == HR)
+    elif kind[i] == LR:
+        ok = (kind == LR) | (kind == TEXT)
+    else:
+        near = (np.maximum(np.abs(wy - wy[i]), np.abs(wx - wx[i])) <= g.radius) & (kind == HR)
+        ok = (kind == TEXT) | (kind == LR) | near
+    return np.nonzero(ok)[0]
+
+
+def allowed_dense(g: Geometry) -> np.ndarray:
+    """Explicit L x L boolean mask (small grids only)."""
+    kind, _, _, wy, wx = token_coords(g)
+    qt, kt = kind[:, None], kind[None, :]
+    hr_near = (np.maximum(np.abs(wy[:, None] - wy[None, :]), np.abs(wx[:, None] - wx[None, :]))
+               <= g.radius) & (qt == HR) & (kt == HR)
+    text_q = (qt == TEXT) & ((kt == TEXT) | (kt == HR))
+    lr_q = (qt == LR) & ((kt == LR) | (kt == TEXT))
+    hr_q = (qt == HR) & ((kt == TEXT) | (kt == LR))
+    return text_q | lr_q | hr_q | hr_near
+
+
+def pair_count(g: Geometry) -> int:
+    """Exact number of allowed (query, key) pairs per head, counted from
+    coordinates one query group at a time."""
+    T, N, Nl = g.n_text, g.n_hr, g.n_lr
+    total = T * (T + N) + Nl * (Nl + T)
+    off = window_offsets(g.hr_h, g.hr_w, g.window)
+    size = np.diff(off)
+    gy, gx = g.grid
+    for a in range(gy):
+        for b in range(gx):
+            seen = 0
+            for a2 in range(max(0, a - g.radius), min(gy, a + g.radius + 1)):
+                for b2 in range(max(0, b - g.radius), min(gx, b + g.radius + 1)):
+                    seen += int(size[a2 * gx + b2])
+            total += int(size[a * gx + b]) * (T + Nl + seen)
+    return total
+
+
+# --------------------------------------------------------------------------
+# Attention ([KD3]: softmax(Q K^T / sqrt(d), masked) V over [C_T; X; X_lr])
+# --------------------------------------------------------------------------
+
+def _softmax_rows(s: np.ndarray) -> np.ndarray:
+    s = s - s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def attention_dense(q, k, v, allowed):
+    """Mode (i): one head, explicit boolean mask; masked logits are -inf."""
+    D = q.shape[1]
+    s = (q @ k.T) / math.sqrt(D)
+    s = np.where(allowed, s, -np.inf)
+    return _softmax_rows(s) @ v
+
+
+def _rows_attention(qr, kr, v, rows, keys):
+    D = qr.shape[1]
+    s = (qr[rows] @ kr[keys].T) / math.sqrt(D)
+    return _softmax_rows(s) @ v[keys]
+
+
+def attention_grouped(g: Geometry, qr, kr, v):
+    """Mode (ii): one head; query rows grouped by the key set they share
+    (text rows, LR rows, HR rows of one window); key indices gathered from
+    coordinates.  qr, kr are already rotated."""
+    coords = token_coords(g)
+    kind, _, _, wy, wx = coords
+    out = np.empty_like(v, dtype=np.float64)
+    T, N = g.n_text, g.n_hr
+    groups = []
+    if T:
+        groups.append(np.arange(T))
+    if g.n_lr:
+        groups.append(np.arange(T + N, g.seq_len))
+    gy, gx = g.grid
+    hr_rows = np.arange(T, T + N)
+    for a in range(gy):
+        for b in range(gx):
+            groups.append(hr_rows[(wy[hr_rows] == a) & (wx[hr_rows] == b)])
+    for rows in groups:
+        if rows.size == 0:
+            continue
+        keys = allowed_keys_of(g, coords, int(rows[0]))
+        out[rows] = _rows_attention(qr, kr, v, rows, keys)
+    return out
+
+
+def rotate_head(g: Geometry, x, theta):
+    """RoPE for every row of one head (text rows stay at position (0, 0))."""
+    _, pr, pc, _, _ = token_coords(g)
+    return rope_rotate(x, pr, pc, theta)
+
+
+def forward_head(g: Geometry, q, k, v, theta, mode="grouped"):
+    """Full path for one head in raster order: RoPE on Q and K, then the
+    composite-masked attention.  q, k, v: [L, D] float64."""
+    qr = rotate_head(g, q, theta)
+    kr = rotate_head(g, k, theta)
+    if mode == "dense":
+        return attention_dense(qr, kr, v, allowed_dense(g))
+    return attention_grouped(g, qr, kr, v)
+
+
+def forward_rows(g: Geometry, q, k, v, theta, rows):
+    """Outputs of selected raster rows of one head (for full-size sampling)."""
+    coords = token_coords(g)
+    _, pr, pc, _, _ = coords
+    rows = np.asarray(rows, np.int64)
+    qr = np.zeros_like(q)
+    qr[rows] = rope_rotate(q[rows], pr[rows], pc[rows], theta)
+    kr = rope_rotate(k, pr, pc, theta)
+    out = np.empty((rows.size, v.shape[1]))
+    for idx, i in enumerate(rows):
+        keys = allowed_keys_of(g, coords, int(i))
+        out[idx] = _rows_attention(qr, kr, v, np.array([i]), keys)[0]
+    return out
