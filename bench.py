@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Benchmark of one hierarchical-local-attention layer on one MI355X.
+
+A step is the whole hot path over one batch of synthetic input already
+resident in HBM: window-first permutation of Q, K and V, 2D axial RoPE on Q
+and K, the composite-masked attention forward, and the inverse permutation of
+O.  The plan (host tables, built once per resolution and reused by every
+layer and denoising step) is built before the timed region.
+
+Prints ONE JSON line.  `value` is effective TFLOP/s of the whole step:
+4 * D * (allowed query-key pairs) * heads / step time, i.e. only unmasked
+pairs count.  Per-kernel times come from HIP events recorded on the stream
+the kernels are launched on (torch's current stream).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (vector / MFMA f32 dense)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "diffusion_transformer_sparse_amd", "csrc", "kernels.hip")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from committed rocprofv3 counters, or
+    None when they were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_sha") != kernel_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle (as it stands) on a bounded sample: whole heads of the
+    same workload, RoPE + grouped composite attention, until `budget_s`."""
+    import numpy as np
+    import workloads as WL
+    from oracle import ultragen_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    geo = O.geometry_of(w)
+    per_head_flops = 4.0 * w.head_dim * O.pair_count(geo)
+    heads, elapsed = 0, 0.0
+    while heads < w.heads and elapsed < budget_s:
+        q, k, v = (WL.head_f64(w, t, heads) for t in (WL.Q, WL.K, WL.V))
+        t0 = time.perf_counter()           # time the oracle call only, not input generation
+        O.forward_head(geo, q, k, v, w.rope_theta)
+        elapsed += time.perf_counter() - t0
+        heads += 1
+    return {"value": per_head_flops * heads / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "sample": f"{heads} of {w.heads} heads of the {w.name} layer "
+                                        f"(fp64 numpy RoPE + grouped masked attention; input generation not timed)",
+            "seconds": round(elapsed, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="4k")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads as WL
+    import diffusion_transformer_sparse_amd as U
+
+    w = WL.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_plan = time.perf_counter()
+    plan = U.ug_plan(U.desc_of(w))
+    t_plan = time.perf_counter() - t_plan
+    info = plan.info
+
+    def to_dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = (to_dev(WL.tensor_storage(w, t)) for t in (WL.Q, WL.K, WL.V))
+    out = torch.empty_like(q)
+    layer = U.Layer(plan, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        U.ug_permute(plan, q, layer.qp)
+        U.ug_permute(plan, k, layer.kp)
+        U.ug_permute(plan, v, layer.vp)
+        if ev is not None:
+            ev[1].record(stream)
+        U.ug_rope2d(plan, layer.qp, layer.kp)
+        if ev is not None:
+            ev[2].record(stream)
+        U.ug_attn_fwd(plan, layer.qp, layer.kp, layer.vp, layer.op)
+        if ev is not None:
+            ev[3].record(stream)
+        U.ug_unpermute(plan, layer.op, out)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+
+    def avg(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in events) / len(events)
+
+    ms_perm3, ms_rope, ms_attn, ms_unperm = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    esize = 2 if w.dtype == "bf16" else 4
+    tbytes = w.batch * w.seq_len * w.heads * w.head_dim * esize
+    rope_bytes = 2 * 2 * w.batch * (w.n_hr + w.n_lr) * w.heads * w.head_dim * esize
+    flops = info["eff_flops"]
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    attn_tflops = flops / (ms_attn * 1e-3) / 1e12
+    traffic = measured_traffic(w.name)
+
+    def gbs(nbytes, ms):
+        return nbytes / (ms * 1e-3) / 1e9
+
+    res = {
+        "metric": "effective attn TFLOP/s + ms/layer at 4K (65,536 HR tok), % of bf16 MFMA peak",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "hr_grid": [w.hr_h, w.hr_w], "lr_grid": [w.lr_h, w.lr_w],
+                   "n_text": w.n_text, "heads": w.heads, "head_dim": w.head_dim, "window": w.window,
+                   "radius": w.radius, "rho": w.rho, "batch": w.batch, "seq_len": w.seq_len,
+                   "pairs_per_head": info["pairs_per_head"], "eff_flop_per_step": flops},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tflops, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
+                     "traffic": traffic},
+        "kernels": {
+            "attn_fwd": {"ms": round(ms_attn, 4), "eff_tflops": round(attn_tflops, 2),
+                         "frac_peak": round(attn_tflops / peak, 4)},
+            "permute_qkv": {"ms": round(ms_perm3, 4), "gbs": round(gbs(3 * 2 * tbytes, ms_perm3), 1),
+                            "frac_hbm": round(gbs(3 * 2 * tbytes, ms_perm3) / PEAK_HBM_GBS, 4)},
+            "rope2d_qk": {"ms": round(ms_rope, 4), "gbs": round(gbs(rope_bytes, ms_rope), 1),
+                          "frac_hbm": round(gbs(rope_bytes, ms_rope) / PEAK_HBM_GBS, 4)},
+            "unpermute_o": {"ms": round(ms_unperm, 4), "gbs": round(gbs(2 * tbytes, ms_unperm), 1),
+                            "frac_hbm": round(gbs(2 * tbytes, ms_unperm) / PEAK_HBM_GBS, 4)},
+        },
+        "plan_build_s": round(t_plan, 4),
+        "kernel_sha": kernel_hash(),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,245 @@
+"""ctypes binding of libultragen.so (the C ABI in include/ultragen.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  torch supplies device memory and the current HIP stream.  The
+library must be built (``python -m diffusion_transformer_sparse_amd.build``);
+there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, byref, c_char_p, c_double, c_int32, c_int64, c_void_p
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libultragen.so")
+
+UG_OK, UG_ERR_INVALID_ARGUMENT, UG_ERR_UNSUPPORTED, UG_ERR_OUT_OF_MEMORY, UG_ERR_HIP, UG_ERR_INTERNAL = range(6)
+UG_F32, UG_BF16 = 0, 1
+UG_PLAN_HOST_ONLY = 1
+
+EXPORTED = ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_permute", "ug_unpermute",
+            "ug_rope2d", "ug_attn_fwd", "ug_status_str", "ug_last_error")
+
+
+class UgDesc(ctypes.Structure):
+    _fields_ = [("batch", c_int32), ("heads", c_int32), ("head_dim", c_int32), ("hr_h", c_int32),
+                ("hr_w", c_int32), ("lr_h", c_int32), ("lr_w", c_int32), ("n_text", c_int32),
+                ("window", c_int32), ("radius", c_int32), ("rho", c_int32), ("dtype", c_int32),
+                ("flags", c_int32), ("reserved", c_int32), ("rope_theta", c_double)]
+
+
+class UgInfo(ctypes.Structure):
+    _fields_ = [("seq_len", c_int64), ("n_hr", c_int64), ("n_lr", c_int64), ("n_text", c_int64),
+                ("grid_y", c_int32), ("grid_x", c_int32), ("n_windows", c_int32), ("max_neighbours", c_int32),
+                ("n_neighbour_entries", c_int64), ("pairs_per_head", c_int64), ("eff_flops", c_double),
+                ("workspace_bytes", c_int64), ("attn_tasks", c_int64), ("attn_blocks", c_int64),
+                ("attn_key_tiles", c_int64), ("rope_positions", c_int64)]
+
+
+class UgError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} -> {status_name(status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libultragen.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m diffusion_transformer_sparse_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.ug_plan.argtypes = [POINTER(UgDesc), POINTER(c_void_p)]
+        L.ug_plan_free.argtypes = [c_void_p]
+        L.ug_plan_info.argtypes = [c_void_p, POINTER(UgInfo)]
+        L.ug_plan_export.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.ug_permute.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
+        L.ug_unpermute.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
+        L.ug_rope2d.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
+        L.ug_attn_fwd.argtypes = [c_void_p] * 7
+        L.ug_status_str.argtypes = [c_int32]
+        L.ug_status_str.restype = c_char_p
+        L.ug_last_error.argtypes = []
+        L.ug_last_error.restype = c_char_p
+        for name in ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_permute", "ug_unpermute",
+                     "ug_rope2d", "ug_attn_fwd"):
+            getattr(L, name).restype = c_int32
+        _lib = L
+    return _lib
+
+
+def status_name(s: int) -> str:
+    return lib().ug_status_str(int(s)).decode()
+
+
+def ug_status_str(s: int) -> str:
+    return status_name(s)
+
+
+def ug_last_error() -> str:
+    return lib().ug_last_error().decode()
+
+
+def _check(fn, status):
+    if status != UG_OK:
+        raise UgError(fn, status, ug_last_error())
+
+
+def make_desc(hr_h, hr_w, lr_h, lr_w, n_text, heads, head_dim, dtype="bf16", window=16, radius=1, rho=4,
+              rope_theta=10000.0, batch=1, host_only=False) -> UgDesc:
+    return UgDesc(batch=batch, heads=heads, head_dim=head_dim, hr_h=hr_h, hr_w=hr_w, lr_h=lr_h, lr_w=lr_w,
+                  n_text=n_text, window=window, radius=radius, rho=rho,
+                  dtype=UG_BF16 if dtype in ("bf16", UG_BF16) else UG_F32,
+                  flags=UG_PLAN_HOST_ONLY if host_only else 0, reserved=0, rope_theta=rope_theta)
+
+
+def desc_of(w, host_only=False) -> UgDesc:
+    """Descriptor of a workloads.Workload (duck-typed)."""
+    return make_desc(w.hr_h, w.hr_w, w.lr_h, w.lr_w, w.n_text, w.heads, w.head_dim, w.dtype, w.window,
+                     w.radius, w.rho, w.rope_theta, w.batch, host_only)
+
+
+class Plan:
+    """Owning handle of a ug_plan_t."""
+
+    def __init__(self, desc: UgDesc):
+        h = c_void_p()
+        _check("ug_plan", lib().ug_plan(byref(desc), byref(h)))
+        self.handle = h
+        self.desc = desc
+        self.info = ug_plan_info(self)
+
+    def close(self):
+        if self.handle:
+            lib().ug_plan_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.close()
+
+    @property
+    def shape(self):
+        d = self.desc
+        return (d.batch, self.info["seq_len"], d.heads, d.head_dim)
+
+
+def ug_plan(desc: UgDesc) -> Plan:
+    return Plan(desc)
+
+
+def ug_plan_free(plan: Plan) -> None:
+    plan.close()
+
+
+def ug_plan_info(plan: Plan) -> dict:
+    info = UgInfo()
+    _check("ug_plan_info", lib().ug_plan_info(plan.handle, byref(info)))
+    return {name: getattr(info, name) for name, _ in UgInfo._fields_}
+
+
+def ug_plan_export(plan: Plan) -> dict:
+    info = plan.info
+    perm = np.empty(info["n_hr"], np.int32)
+    win_off = np.empty(info["n_windows"] + 1, np.int32)
+    nbr = np.empty(max(1, info["n_neighbour_entries"]), np.int32)
+    nbr_off = np.empty(info["n_windows"] + 1, np.int32)
+    _check("ug_plan_export", lib().ug_plan_export(plan.handle, perm.ctypes.data, win_off.ctypes.data,
+                                                  nbr.ctypes.data, nbr_off.ctypes.data))
+    return {"perm": perm, "win_off": win_off, "nbr": nbr[:info["n_neighbour_entries"]], "nbr_off": nbr_off}
+
+
+# ---------------------------------------------------------------- device calls
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(t):
+    torch = _torch()
+    return c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check_tensor(plan: Plan, t, name):
+    torch = _torch()
+    want = torch.bfloat16 if plan.desc.dtype == UG_BF16 else torch.float32
+    if not t.is_cuda or t.dtype != want or not t.is_contiguous() or tuple(t.shape) != plan.shape:
+        raise ValueError(f"{name}: expected a contiguous {want} CUDA tensor of shape {plan.shape}, "
+                         f"got {tuple(t.shape)} {t.dtype} on {t.device} contiguous={t.is_contiguous()}")
+
+
+def ug_permute(plan: Plan, x_raster, x_perm=None):
+    _check_tensor(plan, x_raster, "x_raster")
+    if x_perm is None:
+        x_perm = _torch().empty_like(x_raster)
+    _check_tensor(plan, x_perm, "x_perm")
+    _check("ug_permute", lib().ug_permute(plan.handle, c_void_p(x_raster.data_ptr()), c_void_p(x_perm.data_ptr()),
+                                          _stream_ptr(x_raster)))
+    return x_perm
+
+
+def ug_unpermute(plan: Plan, x_perm, x_raster=None):
+    _check_tensor(plan, x_perm, "x_perm")
+    if x_raster is None:
+        x_raster = _torch().empty_like(x_perm)
+    _check_tensor(plan, x_raster, "x_raster")
+    _check("ug_unpermute", lib().ug_unpermute(plan.handle, c_void_p(x_perm.data_ptr()),
+                                              c_void_p(x_raster.data_ptr()), _stream_ptr(x_perm)))
+    return x_raster
+
+
+def ug_rope2d(plan: Plan, q_perm, k_perm):
+    _check_tensor(plan, q_perm, "q_perm")
+    _check_tensor(plan, k_perm, "k_perm")
+    _check("ug_rope2d", lib().ug_rope2d(plan.handle, c_void_p(q_perm.data_ptr()), c_void_p(k_perm.data_ptr()),
+                                        _stream_ptr(q_perm)))
+    return q_perm, k_perm
+
+
+def ug_attn_fwd(plan: Plan, q, k, v, o=None, workspace=None):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(plan, t, n)
+    if o is None:
+        o = _torch().empty_like(q)
+    _check_tensor(plan, o, "o")
+    ws = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p()
+    _check("ug_attn_fwd", lib().ug_attn_fwd(plan.handle, c_void_p(q.data_ptr()), c_void_p(k.data_ptr()),
+                                            c_void_p(v.data_ptr()), c_void_p(o.data_ptr()), ws, _stream_ptr(q)))
+    return o
+
+
+class Layer:
+    """One attention layer's whole path with preallocated buffers:
+    permute Q, K, V -> RoPE on Q, K -> attention -> unpermute O."""
+
+    def __init__(self, plan: Plan, device="cuda"):
+        torch = _torch()
+        self.plan = plan
+        dt = torch.bfloat16 if plan.desc.dtype == UG_BF16 else torch.float32
+        mk = lambda: torch.empty(plan.shape, dtype=dt, device=device)
+        self.qp, self.kp, self.vp, self.op = mk(), mk(), mk(), mk()
+
+    def __call__(self, q, k, v, out):
+        p = self.plan
+        ug_permute(p, q, self.qp)
+        ug_permute(p, k, self.kp)
+        ug_permute(p, v, self.vp)
+        ug_rope2d(p, self.qp, self.kp)
+        ug_attn_fwd(p, self.qp, self.kp, self.vp, self.op)
+        ug_unpermute(p, self.op, out)
+        return out

@@ -1,0 +1,54 @@
+"""Build the C-ABI shared library libultragen.so in-tree for gfx950.
+
+    python -m diffusion_transformer_sparse_amd.build
+
+Compiles csrc/plan.cpp (host) and csrc/kernels.hip (gfx950 device code) with
+hipcc and links them into diffusion_transformer_sparse_amd/libultragen.so.
+All device code is built with packed-fp32 instructions disabled.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+OUT = os.path.join(HERE, "libultragen.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + os.path.join(ROOT, "include"), "-I/opt/rocm/include"]
+DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-munsafe-fp-atomics"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    plan_o = os.path.join(BUILD_DIR, "plan.o")
+    kern_o = os.path.join(BUILD_DIR, "kernels.o")
+    _run([HIPCC, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, "plan.cpp"),
+          "-o", plan_o], verbose)
+    _run([HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "kernels.hip"), "-o", kern_o], verbose)
+    tmp = OUT + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, plan_o, kern_o, "-o", tmp], verbose)
+    os.replace(tmp, OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,390 @@
+// Host side of the library: descriptor validation, the plan's tables and
+// their upload, info/export, status strings and the thread-local last error.
+//
+// The tables follow UltraGen's hierarchical local attention ("UltraGen:
+// Efficient Ultra-High-Resolution Image Generation with Hierarchical Local
+// Attention", papernotes.org notes, 关键设计 1 and 2):
+//  - window-first order: HR tokens regrouped window by window, windows and
+//    tokens row-major, partial windows at the right/bottom edge of a ragged
+//    grid, compact (no padding);
+//  - neighbourhood: the windows within Chebyshev distance `radius`;
+//  - key ranges: after the window-first permutation every query tile's keys
+//    are a union of contiguous row ranges (text, runs of neighbouring
+//    windows, LR), so the kernel never evaluates a per-element mask;
+//  - RoPE table: cos/sin of pos * theta^(-2k/(D/2)) for every integer
+//    position an HR or scaled LR token can take.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <numeric>
+
+#include "plan_internal.hpp"
+
+namespace ug {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+ug_status fail(ug_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+namespace {
+
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1024;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+ug_status validate(const ug_desc* d) {
+  if (!d) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: desc is NULL");
+  if (d->batch < 1 || d->heads < 1) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: batch and heads must be >= 1");
+  if (d->head_dim < 4 || d->head_dim % 4 != 0)
+    return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: head_dim must be a positive multiple of 4");
+  if (d->hr_h < 1 || d->hr_w < 1) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: hr_h and hr_w must be >= 1");
+  if (d->lr_h < 0 || d->lr_w < 0) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: lr_h and lr_w must be >= 0");
+  if (d->n_text < 0) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: n_text must be >= 0");
+  if (d->window < 1) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: window must be >= 1");
+  if (d->radius < 0) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: radius must be >= 0");
+  if (d->rho < 1) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: rho must be >= 1");
+  if (!(d->rope_theta > 0.0) || !std::isfinite(d->rope_theta))
+    return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: rope_theta must be finite and > 0");
+  if (d->dtype != UG_F32 && d->dtype != UG_BF16) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: unknown dtype");
+  if (d->flags & ~UG_PLAN_HOST_ONLY) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: unknown flags");
+  const int64_t N = int64_t(d->hr_h) * d->hr_w;
+  const int64_t Nlr = int64_t(d->lr_h) * d->lr_w;
+  const int64_t L = int64_t(d->n_text) + N + Nlr;
+  if (L > kMaxRows) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: sequence too long (rows must fit int32)");
+  // largest RoPE position must fit an int32 table index
+  const int64_t maxpos = std::max<int64_t>({int64_t(d->hr_h) - 1, int64_t(d->hr_w) - 1,
+                                            int64_t(d->rho) * std::max(d->lr_h - 1, 0),
+                                            int64_t(d->rho) * std::max(d->lr_w - 1, 0)});
+  if (maxpos > (int64_t(1) << 24)) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: positions too large");
+  if (!(d->flags & UG_PLAN_HOST_ONLY)) {
+    if (d->head_dim != 64 && d->head_dim != 128)
+      return fail(UG_ERR_UNSUPPORTED, "ug_plan: GPU kernels support head_dim 64 or 128");
+    const int64_t rowbytes = int64_t(d->heads) * d->head_dim * (d->dtype == UG_BF16 ? 2 : 4);
+    if (rowbytes % 16 != 0) return fail(UG_ERR_UNSUPPORTED, "ug_plan: heads*head_dim*elem must be a multiple of 16 B");
+  }
+  return UG_OK;
+}
+
+// Window-first order (关键设计 1): slot j of window w = (wy, wx) holds the
+// token at row wy*l + j / hx, column wx*l + j % hx inside the window's hy x hx
+// extent, windows numbered row-major.
+void build_windows(ug_plan_s& p) {
+  const int H = p.d.hr_h, W = p.d.hr_w, l = p.d.window;
+  p.gy = int32_t(ceil_div(H, l));
+  p.gx = int32_t(ceil_div(W, l));
+  p.nwin = p.gy * p.gx;
+  p.perm.resize(p.N);
+  p.inv.resize(p.N);
+  p.win_off.resize(p.nwin + 1);
+  int64_t j = 0;
+  for (int wy = 0; wy < p.gy; ++wy) {
+    const int hy = std::min(l, H - wy * l);
+    for (int wx = 0; wx < p.gx; ++wx) {
+      const int hx = std::min(l, W - wx * l);
+      p.win_off[wy * p.gx + wx] = int32_t(j);
+      for (int ry = 0; ry < hy; ++ry)
+        for (int rx = 0; rx < hx; ++rx) {
+          const int64_t raster = int64_t(wy * l + ry) * W + (wx * l + rx);
+          p.perm[j] = int32_t(raster);
+          p.inv[raster] = int32_t(j);
+          ++j;
+        }
+    }
+  }
+  p.win_off[p.nwin] = int32_t(j);
+  // neighbourhoods: windows within Chebyshev distance `radius`, ascending
+  const int R = p.d.radius;
+  p.nbr.clear();
+  p.nbr_off.assign(p.nwin + 1, 0);
+  p.max_nbr = 0;
+  for (int wy = 0; wy < p.gy; ++wy)
+    for (int wx = 0; wx < p.gx; ++wx) {
+      const int w = wy * p.gx + wx;
+      p.nbr_off[w] = int32_t(p.nbr.size());
+      for (int ay = std::max(0, wy - R); ay <= std::min(p.gy - 1, wy + R); ++ay)
+        for (int ax = std::max(0, wx - R); ax <= std::min(p.gx - 1, wx + R); ++ax) p.nbr.push_back(ay * p.gx + ax);
+      p.max_nbr = std::max<int32_t>(p.max_nbr, int32_t(p.nbr.size()) - p.nbr_off[w]);
+    }
+  p.nbr_off[p.nwin] = int32_t(p.nbr.size());
+}
+
+// RoPE table, double precision rounded to float: cs[pos][k] = (cos, sin) of
+// pos * theta^(-2k/(D/2)), k < D/4.
+void build_rope(ug_plan_s& p) {
+  const int D = p.d.head_dim, K4 = D / 4;
+  int64_t maxpos = std::max(p.d.hr_h, p.d.hr_w) - 1;
+  if (p.Nlr > 0) maxpos = std::max<int64_t>(maxpos, int64_t(p.d.rho) * (std::max(p.d.lr_h, p.d.lr_w) - 1));
+  p.rope_P = int32_t(maxpos + 1);
+  p.rope_cs.resize(size_t(p.rope_P) * K4 * 2);
+  for (int k = 0; k < K4; ++k) {
+    const double omega = std::pow(p.d.rope_theta, -2.0 * k / (D / 2));
+    for (int pos = 0; pos < p.rope_P; ++pos) {
+      const double a = pos * omega;
+      p.rope_cs[(size_t(pos) * K4 + k) * 2 + 0] = float(std::cos(a));
+      p.rope_cs[(size_t(pos) * K4 + k) * 2 + 1] = float(std::sin(a));
+    }
+  }
+}
+
+// Sort and merge key ranges that touch or overlap.
+void push_merged(std::vector<ug::Range>& out, std::vector<ug::Range> rs) {
+  std::sort(rs.begin(), rs.end(), [](const ug::Range& a, const ug::Range& b) { return a.k0 < b.k0; });
+  const size_t base = out.size();
+  for (const auto& r : rs) {
+    if (r.k1 <= r.k0) continue;
+    if (out.size() > base && out.back().k1 >= r.k0)
+      out.back().k1 = std::max(out.back().k1, r.k1);
+    else
+      out.push_back(r);
+  }
+}
+
+int64_t tiles_of(const ug_plan_s& p, const ug::Task& t) {
+  int64_t n = 0;
+  for (int r = t.r0; r < t.r1; ++r) n += ceil_div(p.ranges[r].k1 - p.ranges[r].k0, ug::kAttnKeyTile);
+  return n;
+}
+
+// Query tiles and their key ranges (the composite mask of 关键设计 2):
+//  text rows -> text + HR; LR rows -> text + LR;
+//  HR rows of window w -> text + neighbouring windows + LR.
+void build_tasks(ug_plan_s& p) {
+  const int32_t T = int32_t(p.T), N = int32_t(p.N), L = int32_t(p.L);
+  const int QT = ug::kAttnQueryTile;
+  p.tasks.clear();
+  p.ranges.clear();
+  auto add_rows = [&](int32_t q0, int32_t q1, const std::vector<ug::Range>& rs) {
+    const int32_t r0 = int32_t(p.ranges.size());
+    push_merged(p.ranges, rs);
+    const int32_t r1 = int32_t(p.ranges.size());
+    for (int32_t q = q0; q < q1; q += QT) p.tasks.push_back({q, std::min(q1, q + QT), r0, r1});
+  };
+  if (T > 0) add_rows(0, T, {{0, T + N}});
+  if (p.Nlr > 0) add_rows(T + N, L, {{0, T}, {T + N, L}});
+  for (int w = 0; w < p.nwin; ++w) {
+    std::vector<ug::Range> rs;
+    if (T > 0) rs.push_back({0, T});
+    for (int e = p.nbr_off[w]; e < p.nbr_off[w + 1]; ++e) {
+      const int v = p.nbr[e];
+      rs.push_back({T + p.win_off[v], T + p.win_off[v + 1]});
+    }
+    if (p.Nlr > 0) rs.push_back({T + N, L});
+    add_rows(T + p.win_off[w], T + p.win_off[w + 1], rs);
+  }
+  p.pairs = 0;
+  p.key_tiles = 0;
+  for (const auto& t : p.tasks) {
+    int64_t keys = 0;
+    for (int r = t.r0; r < t.r1; ++r) keys += p.ranges[r].k1 - p.ranges[r].k0;
+    p.pairs += int64_t(t.q1 - t.q0) * keys;
+    p.key_tiles += tiles_of(p, t);
+  }
+}
+
+// Workgroup order.  Hardware hands workgroup i to XCD i % 8, and each XCD has
+// its own L2, so the order is built per XCD: every XCD gets a queue whose
+// long items (query tiles with many more key tiles than the average, i.e.
+// text rows) come first, longest first, then a contiguous slice of the
+// remaining items in (batch, head, tile) order, so that tiles of one head
+// that share neighbour windows and the LR keys run on the same L2.  Queues
+// are balanced by key-tile count and interleaved; short queues are padded
+// with idle workgroups.
+void build_blocks(ug_plan_s& p) {
+  const int64_t BH = int64_t(p.d.batch) * p.d.heads;
+  const int X = ug::kXcds;
+  std::vector<int64_t> cost(p.tasks.size());
+  double mean = 0;
+  for (size_t t = 0; t < p.tasks.size(); ++t) mean += double(cost[t] = tiles_of(p, p.tasks[t]));
+  mean /= double(std::max<size_t>(1, p.tasks.size()));
+  std::vector<int32_t> long_tasks, normal_tasks;
+  for (size_t t = 0; t < p.tasks.size(); ++t)
+    (double(cost[t]) > 2.0 * mean ? long_tasks : normal_tasks).push_back(int32_t(t));
+
+  std::vector<std::vector<ug::Block>> q(X);
+  std::vector<int64_t> load(X, 0);
+  std::vector<ug::Block> longs;
+  for (int64_t bh = 0; bh < BH; ++bh)
+    for (int32_t t : long_tasks) longs.push_back({t, int32_t(bh)});
+  std::stable_sort(longs.begin(), longs.end(),
+                   [&](const ug::Block& a, const ug::Block& b) { return cost[a.task] > cost[b.task]; });
+  for (const auto& b : longs) {
+    const int x = int(std::min_element(load.begin(), load.end()) - load.begin());
+    q[x].push_back(b);
+    load[x] += cost[b.task];
+  }
+  int64_t total = std::accumulate(load.begin(), load.end(), int64_t(0));
+  for (int64_t bh = 0; bh < BH; ++bh)
+    for (int32_t t : normal_tasks) total += cost[t];
+  const double target = double(total) / X;
+  int x = 0;
+  for (int64_t bh = 0; bh < BH; ++bh)
+    for (int32_t t : normal_tasks) {
+      while (x < X - 1 && double(load[x]) >= target) ++x;
+      q[x].push_back({t, int32_t(bh)});
+      load[x] += cost[t];
+    }
+  size_t len = 0;
+  for (const auto& qq : q) len = std::max(len, qq.size());
+  p.blocks.assign(len * X, ug::Block{-1, 0});
+  for (int xx = 0; xx < X; ++xx)
+    for (size_t k = 0; k < q[xx].size(); ++k) p.blocks[k * X + xx] = q[xx][k];
+}
+
+template <typename T>
+ug_status upload(const std::vector<T>& h, T** d) {
+  *d = nullptr;
+  if (h.empty()) return UG_OK;
+  const size_t bytes = h.size() * sizeof(T);
+  if (hipMalloc(reinterpret_cast<void**>(d), bytes) != hipSuccess) {
+    *d = nullptr;
+    (void)hipGetLastError();
+    return fail(UG_ERR_OUT_OF_MEMORY, "ug_plan: hipMalloc of a plan table failed");
+  }
+  if (hipMemcpy(*d, h.data(), bytes, hipMemcpyHostToDevice) != hipSuccess)
+    return fail(UG_ERR_HIP, std::string("ug_plan: hipMemcpy failed: ") + hipGetErrorString(hipGetLastError()));
+  return UG_OK;
+}
+
+void free_device(ug_plan_s* p) {
+  void* ptrs[] = {p->d_perm, p->d_inv, p->d_rope, p->d_tasks, p->d_ranges, p->d_blocks};
+  for (void* q : ptrs)
+    if (q) (void)hipFree(q);
+  p->d_perm = p->d_inv = nullptr;
+  p->d_rope = nullptr;
+  p->d_tasks = nullptr;
+  p->d_ranges = nullptr;
+  p->d_blocks = nullptr;
+}
+
+ug_status check_device(ug_plan_s* p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(UG_ERR_HIP, "ug_plan: no HIP device is available");
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(UG_ERR_HIP, "ug_plan: hipGetDeviceProperties failed");
+  }
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(UG_ERR_UNSUPPORTED, std::string("ug_plan: kernels are built for gfx950, device is ") + prop.gcnArchName);
+  p->device = dev;
+  return UG_OK;
+}
+
+}  // namespace
+}  // namespace ug
+
+extern "C" {
+
+ug_status ug_plan(const ug_desc* desc, ug_plan_t* out) {
+  ug::clear_error();
+  if (!out) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: out is NULL");
+  *out = nullptr;
+  ug_status s = ug::validate(desc);
+  if (s != UG_OK) return s;
+  ug_plan_s* p = new (std::nothrow) ug_plan_s;
+  if (!p) return ug::fail(UG_ERR_OUT_OF_MEMORY, "ug_plan: host allocation failed");
+  try {
+    p->d = *desc;
+    p->host_only = (desc->flags & UG_PLAN_HOST_ONLY) != 0;
+    p->T = desc->n_text;
+    p->N = int64_t(desc->hr_h) * desc->hr_w;
+    p->Nlr = int64_t(desc->lr_h) * desc->lr_w;
+    p->L = p->T + p->N + p->Nlr;
+    ug::build_windows(*p);
+    ug::build_rope(*p);
+    ug::build_tasks(*p);
+    ug::build_blocks(*p);
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return ug::fail(UG_ERR_OUT_OF_MEMORY, "ug_plan: host allocation failed");
+  } catch (...) {
+    delete p;
+    return ug::fail(UG_ERR_INTERNAL, "ug_plan: unexpected exception");
+  }
+  if (!p->host_only) {
+    s = ug::check_device(p);
+    if (s == UG_OK) s = ug::upload(p->perm, &p->d_perm);
+    if (s == UG_OK) s = ug::upload(p->inv, &p->d_inv);
+    if (s == UG_OK) s = ug::upload(p->rope_cs, &p->d_rope);
+    if (s == UG_OK) s = ug::upload(p->tasks, &p->d_tasks);
+    if (s == UG_OK) s = ug::upload(p->ranges, &p->d_ranges);
+    if (s == UG_OK) s = ug::upload(p->blocks, &p->d_blocks);
+    if (s != UG_OK) {
+      ug::free_device(p);
+      delete p;
+      return s;
+    }
+  }
+  *out = p;
+  return UG_OK;
+}
+
+ug_status ug_plan_free(ug_plan_t p) {
+  ug::clear_error();
+  if (!p) return UG_OK;
+  if (!p->host_only) ug::free_device(p);
+  delete p;
+  return UG_OK;
+}
+
+ug_status ug_plan_info(ug_plan_t p, ug_info* out) {
+  ug::clear_error();
+  if (!p || !out) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_plan_info: NULL argument");
+  std::memset(out, 0, sizeof(*out));
+  out->seq_len = p->L;
+  out->n_hr = p->N;
+  out->n_lr = p->Nlr;
+  out->n_text = p->T;
+  out->grid_y = p->gy;
+  out->grid_x = p->gx;
+  out->n_windows = p->nwin;
+  out->max_neighbours = p->max_nbr;
+  out->n_neighbour_entries = int64_t(p->nbr.size());
+  out->pairs_per_head = p->pairs;
+  out->eff_flops = 4.0 * p->d.head_dim * double(p->pairs) * p->d.heads * p->d.batch;
+  out->workspace_bytes = 0;
+  out->attn_tasks = int64_t(p->tasks.size());
+  out->attn_blocks = int64_t(p->blocks.size());
+  out->attn_key_tiles = p->key_tiles;
+  out->rope_positions = p->rope_P;
+  return UG_OK;
+}
+
+ug_status ug_plan_export(ug_plan_t p, int32_t* perm, int32_t* win_off, int32_t* nbr, int32_t* nbr_off) {
+  ug::clear_error();
+  if (!p) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_plan_export: plan is NULL");
+  if (perm) std::memcpy(perm, p->perm.data(), p->perm.size() * sizeof(int32_t));
+  if (win_off) std::memcpy(win_off, p->win_off.data(), p->win_off.size() * sizeof(int32_t));
+  if (nbr && !p->nbr.empty()) std::memcpy(nbr, p->nbr.data(), p->nbr.size() * sizeof(int32_t));
+  if (nbr_off) std::memcpy(nbr_off, p->nbr_off.data(), p->nbr_off.size() * sizeof(int32_t));
+  return UG_OK;
+}
+
+const char* ug_status_str(ug_status s) {
+  switch (s) {
+    case UG_OK: return "UG_OK";
+    case UG_ERR_INVALID_ARGUMENT: return "UG_ERR_INVALID_ARGUMENT";
+    case UG_ERR_UNSUPPORTED: return "UG_ERR_UNSUPPORTED";
+    case UG_ERR_OUT_OF_MEMORY: return "UG_ERR_OUT_OF_MEMORY";
+    case UG_ERR_HIP: return "UG_ERR_HIP";
+    case UG_ERR_INTERNAL: return "UG_ERR_INTERNAL";
+  }
+  return "UG_ERR_UNKNOWN";
+}
+
+const char* ug_last_error(void) { return ug::g_last_error.c_str(); }
+
+}  // extern "C"

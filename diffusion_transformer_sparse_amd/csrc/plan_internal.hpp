@@ -1,0 +1,65 @@
+// Internal plan layout shared by the host plan builder (plan.cpp) and the
+// kernel launchers (kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/ultragen.h"
+
+namespace ug {
+
+// One query tile of the attention: query rows [q0, q1) (at most 256 rows,
+// all sharing one key set) and its key ranges ranges[r0 .. r1).
+struct Task {
+  int32_t q0, q1, r0, r1;
+};
+// A contiguous run of key rows [k0, k1) in the permuted sequence.
+struct Range {
+  int32_t k0, k1;
+};
+// What one workgroup of the attention launch does: query tile `task` of the
+// flattened (batch, head) index `bh`; task < 0 marks an idle workgroup.
+struct Block {
+  int32_t task, bh;
+};
+
+constexpr int kAttnQueryTile = 256;  // query rows per workgroup (8 waves x 32)
+constexpr int kAttnKeyTile = 64;     // key rows per LDS stage
+constexpr int kXcds = 8;             // gfx950: workgroups round-robin over 8 XCDs
+
+}  // namespace ug
+
+struct ug_plan_s {
+  ug_desc d{};
+  int64_t T = 0, N = 0, Nlr = 0, L = 0;
+  int32_t gy = 0, gx = 0, nwin = 0;
+  bool host_only = true;
+  int device = -1;
+
+  // host tables
+  std::vector<int32_t> perm, inv, win_off, nbr, nbr_off;
+  int32_t rope_P = 0;
+  std::vector<float> rope_cs;  // [rope_P][D/4][2]: cos, sin of pos * omega_k
+  std::vector<ug::Task> tasks;
+  std::vector<ug::Range> ranges;
+  std::vector<ug::Block> blocks;
+  int64_t pairs = 0;      // allowed (q, k) pairs per (batch, head)
+  int64_t key_tiles = 0;  // 64-key tiles per (batch, head)
+  int32_t max_nbr = 0;
+
+  // device copies (owned)
+  int32_t* d_perm = nullptr;
+  int32_t* d_inv = nullptr;
+  float* d_rope = nullptr;
+  ug::Task* d_tasks = nullptr;
+  ug::Range* d_ranges = nullptr;
+  ug::Block* d_blocks = nullptr;
+};
+
+namespace ug {
+// thread-local last-error message helpers (plan.cpp)
+ug_status fail(ug_status s, const std::string& msg);
+void clear_error();
+}  // namespace ug

@@ -1,0 +1,173 @@
+/*
+ * ultragen.h -- C ABI of the MI355X (gfx950) hierarchical local attention
+ * library: window-first permutation, 2D axial RoPE with scaled low-resolution
+ * positions, one composite-masked attention forward, inverse permutation.
+ *
+ * The method is UltraGen's ("UltraGen: Efficient Ultra-High-Resolution Image
+ * Generation with Hierarchical Local Attention"; papernotes.org notes,
+ * sections 关键设计 1-3, and the gist.science summary, section 2.A-2.B).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every function is extern "C", never throws, never aborts, and returns a
+ *    ug_status.  Arguments are validated before any HIP call is made; on
+ *    failure nothing is launched and ug_last_error() holds a message
+ *    (thread-local, valid until the next call on the same thread).
+ *  - Tensors Q, K, V, O are device pointers to [B, L, Hh, D] contiguous
+ *    arrays (D innermost), element type = the plan's dtype (fp32 or bf16),
+ *    16-byte aligned.  Rows of one sequence are [text T | HR N | LR N_lr]
+ *    (the joint sequence [C_T; X; X_lr] of 关键设计 3).
+ *      raster layout:   HR row T + r*W + c holds grid token (r, c);
+ *                       LR row T + N + m*w + n holds LR token (m, n).
+ *      permuted layout: HR rows in window-first order (windows row-major,
+ *                       tokens row-major inside a window; partial windows at
+ *                       the bottom/right edges of a ragged grid, no padding);
+ *                       text and LR rows keep their places.
+ *  - The caller owns every tensor and the workspace; the plan owns its own
+ *    device tables.  No entry point allocates device memory except ug_plan.
+ *  - Launches are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Device faults surface at the caller's next synchronisation.
+ *    A plan is immutable after creation and may serve several streams at once.
+ */
+#ifndef ULTRAGEN_H
+#define ULTRAGEN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ug_status {
+  UG_OK = 0,
+  UG_ERR_INVALID_ARGUMENT = 1,  /* bad descriptor, pointer, alignment or aliasing */
+  UG_ERR_UNSUPPORTED = 2,       /* valid request the GPU kernels do not cover */
+  UG_ERR_OUT_OF_MEMORY = 3,     /* host or device allocation failed (ug_plan only) */
+  UG_ERR_HIP = 4,               /* a HIP runtime call or kernel launch failed */
+  UG_ERR_INTERNAL = 5
+} ug_status;
+
+typedef enum ug_dtype { UG_F32 = 0, UG_BF16 = 1 } ug_dtype;
+
+/* ug_desc.flags */
+#define UG_PLAN_HOST_ONLY 1 /* build host tables only: no HIP call; only
+                               ug_plan_info / ug_plan_export / ug_plan_free
+                               may then be used */
+
+/*
+ * Geometry of one attention layer.
+ *  - hr_h x hr_w: HR latent token grid (关键设计 1: X in R^{H x W}).
+ *  - lr_h x lr_w: LR guidance grid (关键设计 2: X_lr in R^{h x w}); given
+ *    explicitly (0 x anything = no LR tokens).  LR token (m, n) takes RoPE
+ *    position (rho*m, rho*n) (关键设计 2, the coordinate-scaling equation).
+ *  - window: l, the window side in tokens (l = 16 in 关键设计 1).  The GPU
+ *    kernels need l*l <= 256.
+ *  - radius: HR queries see HR keys whose window is within Chebyshev
+ *    distance `radius` of their own (1 = own + adjacent windows, 3x3).
+ *  - rope_theta: base of the axial RoPE frequencies omega_k =
+ *    theta^(-2k/(D/2)); dims [0, D/2) are rotated by the row position,
+ *    [D/2, D) by the column position, pairs (2k, 2k+1).
+ *  - GPU kernels support head_dim 64 or 128; dtype UG_BF16 or UG_F32.
+ */
+typedef struct ug_desc {
+  int32_t batch;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t hr_h, hr_w;
+  int32_t lr_h, lr_w;
+  int32_t n_text;
+  int32_t window;
+  int32_t radius;
+  int32_t rho;
+  int32_t dtype; /* ug_dtype */
+  int32_t flags; /* UG_PLAN_* */
+  int32_t reserved;
+  double rope_theta;
+} ug_desc;
+
+typedef struct ug_info {
+  int64_t seq_len;             /* L = T + N + N_lr */
+  int64_t n_hr;                /* N = hr_h * hr_w */
+  int64_t n_lr;                /* lr_h * lr_w */
+  int64_t n_text;              /* T */
+  int32_t grid_y, grid_x;      /* windows per column / row: ceil(H/l), ceil(W/l) */
+  int32_t n_windows;           /* grid_y * grid_x */
+  int32_t max_neighbours;      /* most windows any window sees */
+  int64_t n_neighbour_entries; /* length of the exported neighbour list */
+  int64_t pairs_per_head;      /* exact number of allowed (query, key) pairs */
+  double eff_flops;            /* 4 * D * pairs_per_head * heads * batch */
+  int64_t workspace_bytes;     /* bytes ug_attn_fwd needs as workspace (0 today) */
+  int64_t attn_tasks;          /* query tiles per (batch, head) */
+  int64_t attn_blocks;         /* workgroups one ug_attn_fwd launches */
+  int64_t attn_key_tiles;      /* 64-key tiles processed per (batch, head) */
+  int64_t rope_positions;      /* rows of the RoPE cos/sin table */
+} ug_info;
+
+typedef struct ug_plan_s* ug_plan_t;
+
+/*
+ * ug_plan: validate `desc`, build the host tables (window-first permutation
+ * and inverse, window offsets, window neighbourhoods, the per-query-tile key
+ * range list and workgroup order, RoPE cos/sin table computed in double and
+ * stored as float) and, unless UG_PLAN_HOST_ONLY, upload them to the current
+ * HIP device (synchronous).  The window-first order is 关键设计 1's regrouping
+ * of tokens window by window; the neighbourhood is its adjacent-window
+ * interaction.  On success *out owns everything; free it with ug_plan_free
+ * once no launched work still uses it.
+ */
+ug_status ug_plan(const ug_desc* desc, ug_plan_t* out);
+ug_status ug_plan_free(ug_plan_t plan);
+ug_status ug_plan_info(ug_plan_t plan, ug_info* out);
+
+/*
+ * ug_plan_export: host copies of the plan's integer tables, for inspection
+ * and bit-exact tests.  Any pointer may be NULL to skip that table.
+ *  perm    int32[N]            perm[j] = raster HR index of window-first slot j
+ *  win_off int32[n_windows+1]  window w occupies slots [win_off[w], win_off[w+1])
+ *  nbr     int32[n_neighbour_entries]  windows (ascending) each window sees
+ *  nbr_off int32[n_windows+1]  window w's list is nbr[nbr_off[w] .. nbr_off[w+1])
+ */
+ug_status ug_plan_export(ug_plan_t plan, int32_t* perm, int32_t* win_off, int32_t* nbr,
+                         int32_t* nbr_off);
+
+/*
+ * ug_permute: x_perm = x_raster with HR rows gathered into window-first
+ * order (关键设计 1; gist.science summary 2.A, window-first token
+ * permutation); text and LR rows copied unchanged.  Out of place:
+ * x_raster == x_perm (or any overlap) is UG_ERR_INVALID_ARGUMENT.
+ * ug_unpermute is the exact inverse (bit copies both ways).
+ */
+ug_status ug_permute(ug_plan_t plan, const void* x_raster, void* x_perm, void* stream);
+ug_status ug_unpermute(ug_plan_t plan, const void* x_perm, void* x_raster, void* stream);
+
+/*
+ * ug_rope2d: in place on permuted Q and K, rotate every HR and LR row by its
+ * 2D position (HR: grid (r, c); LR: (rho*m, rho*n), 关键设计 2); text rows are
+ * left unchanged (position (0, 0)).  Math in fp32, bf16 results rounded to
+ * nearest even.  q_perm and k_perm must not overlap.
+ */
+ug_status ug_rope2d(ug_plan_t plan, void* q_perm, void* k_perm, void* stream);
+
+/*
+ * ug_attn_fwd: O = softmax(Q K^T / sqrt(D) + M) V per (batch, head) on
+ * permuted, rotated Q and K and permuted V (关键设计 3's joint attention over
+ * [C_T; X; X_lr]).  M is the composite mask of 关键设计 2: a text query sees
+ * text and HR keys; an HR query sees text, all LR, and the HR keys of its own
+ * and adjacent windows; an LR query sees LR and text.  Masked keys are
+ * excluded (additive -inf).  O is written in the permuted layout.  bf16: bf16
+ * MFMA products, fp32 softmax and accumulation, O rounded to nearest even;
+ * fp32: fp32 MFMA throughout.  `workspace` may be NULL when
+ * info.workspace_bytes is 0.  o must not overlap q, k or v.
+ */
+ug_status ug_attn_fwd(ug_plan_t plan, const void* q, const void* k, const void* v, void* o,
+                      void* workspace, void* stream);
+
+const char* ug_status_str(ug_status s);
+const char* ug_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ULTRAGEN_H */

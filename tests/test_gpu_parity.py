@@ -1,0 +1,221 @@
+"""GPU parity: every entry point of the C ABI (through the Python binding)
+against the fp64 oracle on the same seeded inputs.
+
+Bars: permutation bit-exact; bf16 attention max-abs <= 2e-2 and rel-L2 <=
+5e-3 per segment (text / HR / LR rows) and head; fp32 1e-4 for both.
+"""
+import numpy as np
+import pytest
+
+import workloads as WL
+from oracle import ultragen_oracle as O
+from tests.gpu_util import (assert_close, qkv_device, seg_errors, to_device, to_host_f64, to_host_storage,
+                            tol_of)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["tiny", "tiny_masked", "small_ragged", "small_d64", "small_ragged_f32", "1k"]
+
+
+@pytest.fixture(scope="module")
+def U():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import diffusion_transformer_sparse_amd as U
+    return U
+
+
+def plan_of(U, w):
+    return U.ug_plan(U.desc_of(w))
+
+
+def expected_permuted(w, x):
+    """Host gather with the oracle's window-first order (rows of all heads)."""
+    perm = O.window_first_perm(w.hr_h, w.hr_w, w.window)
+    T, N = w.n_text, w.n_hr
+    out = x.copy()
+    out[:, T:T + N] = x[:, T + perm]
+    return out
+
+
+# ------------------------------------------------------------------ permutation
+
+@pytest.mark.parametrize("name", ["tiny", "small_ragged", "small_ragged_f32", "1k", "ragged", "4k"])
+def test_permute_unpermute_bit_exact(U, name):
+    import torch
+    w = WL.WORKLOADS[name]
+    x = WL.tensor_storage(w, WL.V)
+    p = plan_of(U, w)
+    xd = to_device(x, w.dtype)
+    xp = U.ug_permute(p, xd)
+    back = U.ug_unpermute(p, xp)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_storage(xp, w.dtype), expected_permuted(w, x))
+    assert np.array_equal(to_host_storage(back, w.dtype), x)
+
+
+# ------------------------------------------------------------------ RoPE
+
+@pytest.mark.parametrize("name", ["tiny", "small_ragged", "small_d64", "small_ragged_f32", "1k"])
+def test_rope2d_matches_oracle(U, name):
+    import torch
+    w = WL.WORKLOADS[name]
+    p = plan_of(U, w)
+    q, k, _ = qkv_device(w)
+    qp, kp = U.ug_permute(p, q), U.ug_permute(p, k)
+    text_before = qp[:, :w.n_text].clone()
+    U.ug_rope2d(p, qp, kp)
+    torch.cuda.synchronize()
+    assert torch.equal(qp[:, :w.n_text], text_before)
+    geo = O.geometry_of(w)
+    perm = O.window_first_perm(w.hr_h, w.hr_w, w.window)
+    T, N = w.n_text, w.n_hr
+    order = np.concatenate([np.arange(T), T + perm, np.arange(T + N, w.seq_len)])
+    for t, dev in ((WL.Q, qp), (WL.K, kp)):
+        got = to_host_f64(dev, w.dtype)[0]
+        for h in range(w.heads):
+            ref = O.rotate_head(geo, WL.head_f64(w, t, h), w.rope_theta)[order]
+            err = np.abs(got[:, h] - ref)
+            if w.dtype == "bf16":   # fp32 math, one round to nearest bf16
+                assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-6), float(err.max())
+            else:
+                assert np.all(err <= 1e-6 * np.abs(ref) + 2e-6), float(err.max())
+
+
+# ------------------------------------------------------------------ attention
+
+def run_attn_only(U, w):
+    """permute -> attention (no RoPE) -> unpermute, result [L, Hh, D] float64."""
+    import torch
+    p = plan_of(U, w)
+    q, k, v = qkv_device(w)
+    qp, kp, vp = (U.ug_permute(p, x) for x in (q, k, v))
+    o = U.ug_unpermute(p, U.ug_attn_fwd(p, qp, kp, vp))
+    torch.cuda.synchronize()
+    return to_host_f64(o, w.dtype)[0]
+
+
+def oracle_attn_only(w, h):
+    geo = O.geometry_of(w)
+    return O.attention_grouped(geo, WL.head_f64(w, WL.Q, h), WL.head_f64(w, WL.K, h), WL.head_f64(w, WL.V, h))
+
+
+@pytest.mark.parametrize("name,qscale", [(n, 1.0) for n in SMALL] + [("small_ragged", 8.0), ("1k", 8.0),
+                                                                    ("tiny_masked", 8.0)])
+def test_attention_matches_oracle(U, name, qscale):
+    w = WL.WORKLOADS[name].with_(q_scale=qscale)
+    got = run_attn_only(U, w)
+    for h in range(w.heads):
+        assert_close(seg_errors(got[:, h], oracle_attn_only(w, h), w), tol_of(w), f"{name} x{qscale} head {h}")
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_full_layer_matches_oracle(U, name):
+    import torch
+    w = WL.WORKLOADS[name]
+    p = plan_of(U, w)
+    q, k, v = qkv_device(w)
+    out = torch.empty_like(q)
+    U.Layer(p)(q, k, v, out)
+    torch.cuda.synchronize()
+    got = to_host_f64(out, w.dtype)[0]
+    geo = O.geometry_of(w)
+    for h in range(w.heads):
+        ref = O.forward_head(geo, *(WL.head_f64(w, t, h) for t in (WL.Q, WL.K, WL.V)), w.rope_theta)
+        assert_close(seg_errors(got[:, h], ref, w), tol_of(w), f"{name} head {h}")
+
+
+def sample_rows(w, seed=0):
+    rng = np.random.default_rng(seed)
+    T, N, L, H, W = w.n_text, w.n_hr, w.seq_len, w.hr_h, w.hr_w
+    rows = [0, T - 1, T // 2] if T else []
+    pts = [(0, 0), (0, W - 1), (H - 1, 0), (H - 1, W - 1), (15, 16), (16, 15), (H // 2, W // 2),
+           (min(31, H - 1), min(47, W - 1)), (H - 1, W // 3)]
+    rows += [T + r * W + c for r, c in pts]
+    rows += list(T + rng.integers(0, N, 12))
+    if w.n_lr:
+        rows += [T + N, L - 1] + list(T + N + rng.integers(0, w.n_lr, 4))
+    return np.unique(np.asarray(rows, np.int64))
+
+
+@pytest.mark.parametrize("name", ["2k", "ragged", "4k", "8k"])
+def test_full_size_sampled_rows(U, name):
+    """The bench's launch configuration at full size; the oracle recomputes
+    sampled rows one by one (text, corner/edge/interior HR windows, LR)."""
+    import torch
+    w = WL.WORKLOADS[name]
+    p = plan_of(U, w)
+    q, k, v = qkv_device(w)
+    out = torch.empty_like(q)
+    U.Layer(p)(q, k, v, out)
+    torch.cuda.synchronize()
+    geo = O.geometry_of(w)
+    rows = sample_rows(w)
+    for h in (0, w.heads - 1):
+        got = to_host_f64(out[0, rows, h], w.dtype)
+        ref = O.forward_rows(geo, *(WL.head_f64(w, t, h) for t in (WL.Q, WL.K, WL.V)), w.rope_theta, rows)
+        assert_close(seg_errors(got, ref, w, rows), tol_of(w), f"{name} head {h}")
+    assert torch.isfinite(out.float()).all()
+
+
+def test_attention_is_deterministic(U):
+    import torch
+    w = WL.WORKLOADS["1k"]
+    p = plan_of(U, w)
+    q, k, v = qkv_device(w)
+    o1 = U.ug_attn_fwd(p, q, k, v)
+    o2 = U.ug_attn_fwd(p, q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+# ------------------------------------------------------------------ edge cases
+
+EDGE = {
+    "no_text": dict(n_text=0),
+    "no_lr": dict(lr_h=0, lr_w=0),
+    "no_text_no_lr": dict(n_text=0, lr_h=0, lr_w=0),
+    "radius0": dict(radius=0),
+    "radius2": dict(radius=2),
+    "window8": dict(window=8),
+    "window_covers_grid": dict(window=64),
+    "batch2": dict(batch=2),
+    "one_text": dict(n_text=1),
+}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", list(EDGE))
+def test_edge_cases(U, case, dtype):
+    import torch
+    base = WL.WORKLOADS["small_ragged_f32"].with_(dtype=dtype, cfg_id=20)
+    w = base.with_(**EDGE[case])
+    p = plan_of(U, w)
+    q, k, v = qkv_device(w)
+    out = torch.empty_like(q)
+    U.Layer(p)(q, k, v, out)
+    torch.cuda.synchronize()
+    geo = O.geometry_of(w)
+    for b in range(w.batch):
+        got = to_host_f64(out[b], w.dtype)
+        for h in range(w.heads):
+            ref = O.forward_head(geo, *(WL.head_f64(w, t, h, b) for t in (WL.Q, WL.K, WL.V)), w.rope_theta)
+            assert_close(seg_errors(got[:, h], ref, w), tol_of(w), f"{case} {dtype} b{b} h{h}")
+
+
+def test_argument_errors_on_device(U):
+    import torch
+    w = WL.WORKLOADS["tiny"]
+    p = plan_of(U, w)
+    q, k, v = qkv_device(w)
+    lib = U.lib()
+    import ctypes
+    vp = ctypes.c_void_p
+    s = vp(torch.cuda.current_stream().cuda_stream)
+    assert lib.ug_permute(p.handle, vp(q.data_ptr()), vp(q.data_ptr()), s) == 1
+    assert lib.ug_permute(p.handle, vp(q.data_ptr() + 4), vp(k.data_ptr()), s) == 1
+    assert lib.ug_attn_fwd(p.handle, vp(q.data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()), vp(q.data_ptr()),
+                           None, s) == 1
+    assert lib.ug_rope2d(p.handle, vp(q.data_ptr()), vp(q.data_ptr()), s) == 1
+    with pytest.raises(ValueError):
+        U.ug_permute(p, q[:, :10].contiguous())

@@ -1,0 +1,121 @@
+"""Host-side tests of the C-ABI library (no GPU): symbol exports, descriptor
+validation, and bit-exact plan tables against the oracle's coordinate-derived
+window-first order, window offsets and neighbourhoods."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import diffusion_transformer_sparse_amd as U
+from oracle import ultragen_oracle as O
+from workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "ultragen.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\*\s]+?\b(ug_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = header_functions()
+    assert set(names) == set(U.EXPORTED), names
+    lib = ctypes.CDLL(U.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert U.ug_status_str(0) == "UG_OK"
+    assert U.ug_status_str(1) == "UG_ERR_INVALID_ARGUMENT"
+    assert U.ug_status_str(4) == "UG_ERR_HIP"
+
+
+def _host_plan(w):
+    return U.ug_plan(U.desc_of(w, host_only=True))
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_plan_tables_bit_exact(name):
+    w = WORKLOADS[name]
+    p = _host_plan(w)
+    t = U.ug_plan_export(p)
+    assert np.array_equal(t["perm"], O.window_first_perm(w.hr_h, w.hr_w, w.window))
+    assert np.array_equal(t["win_off"], O.window_offsets(w.hr_h, w.hr_w, w.window))
+    nbr, off = O.neighbour_windows(w.hr_h, w.hr_w, w.window, w.radius)
+    assert np.array_equal(t["nbr"], nbr) and np.array_equal(t["nbr_off"], off)
+    geo = O.geometry_of(w)
+    info = p.info
+    assert info["pairs_per_head"] == O.pair_count(geo)
+    assert info["seq_len"] == geo.seq_len and info["n_lr"] == geo.n_lr
+    assert info["eff_flops"] == 4.0 * w.head_dim * info["pairs_per_head"] * w.heads * w.batch
+    p.close()
+
+
+@pytest.mark.parametrize("H,W,l,r,T,lh,lw", [(3, 5, 2, 1, 2, 1, 2), (17, 33, 16, 1, 0, 5, 9), (40, 40, 8, 2, 7, 0, 0),
+                                              (64, 48, 32, 1, 5, 16, 12), (20, 20, 64, 0, 3, 5, 5),
+                                              (33, 65, 16, 0, 0, 9, 17)])
+def test_plan_odd_geometries(H, W, l, r, T, lh, lw):
+    d = U.make_desc(H, W, lh, lw, T, 2, 64, "f32", window=l, radius=r, host_only=True)
+    p = U.ug_plan(d)
+    t = U.ug_plan_export(p)
+    assert np.array_equal(t["perm"], O.window_first_perm(H, W, l))
+    assert np.array_equal(t["win_off"], O.window_offsets(H, W, l))
+    nbr, off = O.neighbour_windows(H, W, l, r)
+    assert np.array_equal(t["nbr"], nbr) and np.array_equal(t["nbr_off"], off)
+    geo = O.Geometry(H, W, lh, lw, T, l, r, 4)
+    assert p.info["pairs_per_head"] == O.pair_count(geo) == int(O.allowed_dense(geo).sum())
+
+
+def test_rope_table_rows_cover_scaled_lr_positions():
+    w = WORKLOADS["ragged"]
+    p = _host_plan(w)
+    assert p.info["rope_positions"] == max(w.hr_h, w.hr_w, 4 * (w.lr_h - 1) + 1, 4 * (w.lr_w - 1) + 1)
+    w2 = w.with_(lr_h=80, lr_w=120)   # LR grid reaching past the HR grid
+    p2 = _host_plan(w2)
+    assert p2.info["rope_positions"] == 4 * 119 + 1
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, U.UgError), ("heads", 0, U.UgError), ("head_dim", 6, U.UgError), ("hr_h", 0, U.UgError),
+    ("lr_w", -1, U.UgError), ("n_text", -3, U.UgError), ("window", 0, U.UgError), ("radius", -1, U.UgError),
+    ("rho", 0, U.UgError), ("dtype", 7, U.UgError), ("flags", 8, U.UgError), ("rope_theta", -1.0, U.UgError)])
+def test_descriptor_validation(field, value, status):
+    d = U.desc_of(WORKLOADS["tiny"], host_only=True)
+    setattr(d, field, value)
+    with pytest.raises(status) as e:
+        U.ug_plan(d)
+    assert e.value.status == 1  # UG_ERR_INVALID_ARGUMENT
+    assert "ug_plan" in U.ug_last_error()
+
+
+def test_host_only_plan_rejects_device_calls():
+    p = _host_plan(WORKLOADS["tiny"])
+    lib = U.lib()
+    st = lib.ug_permute(p.handle, ctypes.c_void_p(16), ctypes.c_void_p(4096), None)
+    assert st == 1 and "host-only" in U.ug_last_error()
+    st = lib.ug_attn_fwd(p.handle, *(ctypes.c_void_p(16 * (i + 1)) for i in range(4)), None, None)
+    assert st == 1
+    st = lib.ug_permute(None, ctypes.c_void_p(16), ctypes.c_void_p(4096), None)
+    assert st == 1 and "NULL" in U.ug_last_error()
+
+
+def test_null_arguments():
+    lib = U.lib()
+    assert lib.ug_plan(None, None) == 1
+    assert lib.ug_plan_info(None, None) == 1
+    assert lib.ug_plan_free(None) == 0
+
+
+def test_block_order_covers_every_task_once():
+    """Every (task, batch*head) pair appears exactly once in the workgroup order;
+    the rest of the entries are idle."""
+    w = WORKLOADS["4k"]
+    p = _host_plan(w)
+    info = p.info
+    assert info["attn_blocks"] >= info["attn_tasks"] * w.heads
+    assert info["attn_blocks"] - info["attn_tasks"] * w.heads < 8 * 64
