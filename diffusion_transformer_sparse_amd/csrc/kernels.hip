@@ -155,9 +155,10 @@ __global__ __launch_bounds__(kRopeThreads) void rope2d_kernel(T* __restrict__ q,
 // Composite-masked attention forward (关键设计 3 with the mask of 关键设计 2).
 //
 // One workgroup = one query tile (<= 256 permuted rows sharing one key set)
-// of one (batch, head); 8 waves x 32 queries.  The key set is a list of
-// contiguous row ranges, walked in 64-key tiles staged through LDS (double
-// buffered, one barrier per tile).
+// of one (batch, head); 8 waves x 32 queries, two waves per SIMD.  The key
+// set is a list of contiguous row ranges, walked in 64-key tiles that go
+// straight from global memory into LDS (global_load_lds_dwordx4, no
+// registers), one barrier per tile.
 //
 // Per wave and 64-key tile, with 32x32 MFMA tiles (lane l: column l%32,
 // lane half g = l/32):
@@ -165,19 +166,30 @@ __global__ __launch_bounds__(kRopeThreads) void rope2d_kernel(T* __restrict__ q,
 //                  Output lane l holds query l%32 and 16 keys
 //                  8*(j/4) + 4*g + j%4 (j < 16) of each 32-key block, so a
 //                  query's softmax statistics are lane-local except for one
-//                  exchange between the two lane halves.
+//                  exchange between the two lane halves (v_permlane32_swap).
 //   P = exp2(S*scale*log2e - m), m the running maximum (fp32).
-//   O^T += V^T P^T A = V^T from LDS, B = P^T straight from the S^T
-//                  registers.  V is stored transposed in LDS with its 4-key
-//                  groups reordered so that each lane's 8 B-operand keys are
-//                  the 8 keys its S^T registers hold: no register shuffles.
-// The running maximum is only moved when a tile's maximum exceeds it by more
-// than 8 (log2 units); the final normalisation uses the same reference, so
-// the result is unchanged while the 64 O^T registers are rescaled rarely.
-// bf16: v_mfma_f32_32x32x16_bf16, P rounded to bf16 for the PV product and
-// the row sum taken over the same rounded P; fp32: v_mfma_f32_32x32x2_f32.
+//   O^T += V^T P^T A = V^T read from the [key][dim] V tile with the LDS
+//                  transpose read ds_read_b64_tr_b16: in each 16-lane group,
+//                  lane j gets dim j of four keys, so two reads give a lane
+//                  the 8 keys its own S^T registers hold (keys 4g..4g+3 and
+//                  8+4g..8+4g+3 of a 16-key chunk): B = P^T straight from
+//                  the S^T registers, no shuffles.
+// LDS rows are unpadded; 16-byte chunks are XOR-swizzled by row so the
+// K-operand reads (32 rows, one chunk) and the transpose reads (4 rows,
+// 64 bytes) are bank-conflict free.
+// Software pipeline: K runs one tile ahead of V in two LDS rings, so while a
+// wave exponentiates tile i's scores (VALU) it already issues tile i+1's
+// QK^T MFMAs, then tile i's PV MFMAs; the MFMA and VALU pipes overlap inside
+// one wave.  The running maximum is only moved when a tile's maximum exceeds
+// it by more than 8 (log2 units); the final normalisation uses the same
+// reference, so the result is unchanged while the O^T registers are
+// rescaled rarely.  bf16: v_mfma_f32_32x32x16_bf16, P rounded to bf16 for
+// the PV product and the row sum taken over the same rounded P; fp32:
+// v_mfma_f32_32x32x2_f32.  The output goes through LDS so every row is
+// written with full 16-byte stores.
 // ---------------------------------------------------------------------------
 constexpr int kAttnThreads = 512;
+constexpr int kAttnWaves = kAttnThreads / 64;
 constexpr int kKT = ug::kAttnKeyTile;  // 64
 
 struct AttnParams {
@@ -195,32 +207,137 @@ struct AttnParams {
   float scale_log2;      // log2(e) / sqrt(D)
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
 template <typename T, int D>
 struct AttnLds {
   static constexpr bool kBF = std::is_same<T, __bf16>::value;
-  // K rows [key][dim], padded by 16 bytes so 32 lanes reading 32 rows hit
-  // distinct banks.
-  static constexpr int kKStride = D + 16 / int(sizeof(T));
-  // bf16: V^T rows [dim][key position]; fp32: V rows [key][dim].
-  static constexpr int kVStride = kBF ? (kKT + 8) : (D + 4);
-  static constexpr int kKElems = kKT * kKStride;
-  static constexpr int kVElems = kBF ? D * kVStride : kKT * kVStride;
-  static constexpr int kStageElems = kKElems + kVElems;
-  static constexpr int kBytes = 2 * kStageElems * int(sizeof(T));
-  // staging work per thread
-  static constexpr int kKChunks = kKT * D * int(sizeof(T)) / 16;      // 16-B chunks of K
-  static constexpr int kKPerThread = (kKChunks + kAttnThreads - 1) / kAttnThreads;
-  static constexpr int kVUnits = kBF ? (kKT / 4) * (D / 4) : kKChunks;  // bf16: 4 keys x 4 dims
-  static constexpr int kVPerThread = (kVUnits + kAttnThreads - 1) / kAttnThreads;
+  static constexpr int kEl16 = 16 / int(sizeof(T));  // elements per 16-B chunk
+  static constexpr int kChunks = D / kEl16;           // chunks per row
+  static_assert(kChunks == 8 || kChunks == 16 || kChunks == 32, "row must be 8, 16 or 32 chunks");
+  static constexpr int kTileBytes = kKT * D * int(sizeof(T));
+  static constexpr int kSlots = kTileBytes / 16;      // 16-B slots per tile
+  static constexpr int kLoadsPerThread = kSlots / kAttnThreads;
+  static_assert(kSlots % kAttnThreads == 0, "tile must split evenly over the workgroup");
+  static constexpr int kTotalBytes = 4 * kTileBytes;  // K ring (2) + V ring (2)
+  static_assert(kAttnWaves * 32 * D * int(sizeof(T)) <= kTotalBytes, "output staging must fit");
+  // physical chunk of logical chunk c in row r
+  __device__ static __forceinline__ int k_swz(int r) {  // 16 consecutive rows -> 16 bank groups
+    if constexpr (kChunks >= 16) return r & 15;
+    else return (r >> 1) & 7;
+  }
+  __device__ static __forceinline__ int v_swz(int r) {  // 4 consecutive rows x 4 chunks -> 16 bank groups
+    if constexpr (kChunks >= 16) return 4 * (r & 3);
+    else return 4 * ((r >> 1) & 1);
+  }
 };
 
-__device__ __forceinline__ float wave_other_half(float x) { return __shfl_xor(x, 32); }
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Walks the 64-key tiles of a query tile's key ranges.
+struct TileCursor {
+  int32_t ri, r1, ks, k1;
+  __device__ __forceinline__ void init(const ug::Range* ranges, int32_t r0, int32_t rend) {
+    ri = r0;
+    r1 = rend;
+    const ug::Range r = ranges[r0];
+    ks = r.k0;
+    k1 = r.k1;
+  }
+  __device__ __forceinline__ int32_t nv() const { return min(kKT, k1 - ks); }
+  __device__ __forceinline__ void advance(const ug::Range* ranges) {
+    ks += kKT;
+    if (ks >= k1 && ri + 1 < r1) {
+      ++ri;
+      const ug::Range r = ranges[ri];
+      ks = r.k0;
+      k1 = r.k1;
+    }
+  }
+};
+
+// Direct global->LDS loads of one 64-key tile (rows ks .. ks+63).  Slot
+// s = i*512 + tid of the tile holds row s / kChunks, physical chunk
+// s % kChunks, i.e. logical chunk (s % kChunks) ^ swz(row).  `off[i]` is the
+// thread's byte offset of that chunk relative to row ks (constant over
+// tiles); a ragged tile (nv < 64) repeats its last row instead (those scores
+// are masked), so no load leaves the key range.
+template <typename T, int D, bool kIsV>
+struct TileLoader {
+  using Lds = AttnLds<T, D>;
+  uint32_t off[Lds::kLoadsPerThread];
+  __device__ __forceinline__ static int row_of(int i, int tid) { return (i * kAttnThreads + tid) / Lds::kChunks; }
+  __device__ __forceinline__ static int lchunk_of(int i, int tid) {
+    const int slot = i * kAttnThreads + tid;
+    const int r = slot / Lds::kChunks;
+    return (slot % Lds::kChunks) ^ (kIsV ? Lds::v_swz(r) : Lds::k_swz(r));
+  }
+  __device__ __forceinline__ void init(int64_t rs, int tid) {
+#pragma unroll
+    for (int i = 0; i < Lds::kLoadsPerThread; ++i)
+      off[i] = uint32_t(row_of(i, tid) * rs * int64_t(sizeof(T)) + lchunk_of(i, tid) * 16);
+  }
+  __device__ __forceinline__ void issue(const T* __restrict__ src, int64_t rs, int32_t ks, int32_t nv, char* tile,
+                                        int tid, int wave) const {
+    const char* base = reinterpret_cast<const char*>(src + int64_t(ks) * rs);  // wave-uniform
+    if (nv == kKT) {
+#pragma unroll
+      for (int i = 0; i < Lds::kLoadsPerThread; ++i)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(base + off[i]),
+                                         (lds_void*)(tile + (i * kAttnThreads + wave * 64) * 16), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < Lds::kLoadsPerThread; ++i) {
+        const int r = min(row_of(i, tid), nv - 1);
+        const char* gp = base + int64_t(r) * rs * int64_t(sizeof(T)) + lchunk_of(i, tid) * 16;
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(gp),
+                                         (lds_void*)(tile + (i * kAttnThreads + wave * 64) * 16), 16, 0, 0);
+      }
+    }
+  }
+};
+
+// S^T (two 32-key blocks) = K Q^T for one 64-key tile in LDS.  koff[i] is
+// the lane's byte offset of its chunk for MFMA step i in row l%32.
+template <typename T, int D, typename QReg, int KOFF>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const char* ktile, const QReg* qf, const int (&koff)[KOFF]) {
+  using Lds = AttnLds<T, D>;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const char* kb = ktile + mb * 32 * D * int(sizeof(T));
+    if constexpr (Lds::kBF) {
+      s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kb + koff[0]), qf[0],
+                                                      f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int i = 1; i < D / 16; ++i)
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kb + koff[i]), qf[i],
+                                                        s[mb], 0, 0, 0);
+    } else {
+      s[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(*reinterpret_cast<const float*>(kb + koff[0]), qf[0], f32x16{},
+                                                   0, 0, 0);
+#pragma unroll
+      for (int i = 1; i < D / 2; ++i)
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(*reinterpret_cast<const float*>(kb + koff[i]), qf[i], s[mb], 0,
+                                                     0, 0);
+    }
+  }
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
   using Lds = AttnLds<T, D>;
   constexpr bool kBF = Lds::kBF;
-  __shared__ __attribute__((aligned(16))) T smem[2 * Lds::kStageElems];
+  constexpr int TB = Lds::kTileBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[Lds::kTotalBytes];
+  // K ring at [0, 2*TB), V ring at [2*TB, 4*TB)
 
   const ug::Block blk = p.blocks[blockIdx.x];
   if (blk.task < 0) return;  // idle workgroup (uniform)
@@ -237,9 +354,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int32_t qrow = task.q0 + wave * 32 + l32;
-  const bool qvalid = qrow < task.q1;
-  const bool wave_active = task.q0 + wave * 32 < task.q1;  // uniform per wave
-  const int32_t qload = qvalid ? qrow : task.q1 - 1;
+  const int32_t qload = qrow < task.q1 ? qrow : task.q1 - 1;
+  const float c2 = p.scale_log2;
+
+  // number of 64-key tiles
+  int32_t ntiles = 0;
+  for (int32_t r = task.r0; r < task.r1; ++r) {
+    const ug::Range rg = p.ranges[r];
+    ntiles += (rg.k1 - rg.k0 + kKT - 1) / kKT;
+  }
 
   // The wave's queries as the B operand of S^T = K Q^T.
   constexpr int kQRegs = kBF ? D / 16 : D / 2;
@@ -253,141 +376,94 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
       qf[i] = qg[qload * rs + 2 * i + g];
   }
 
+  // Per-lane LDS byte offsets.  K operand of step i: row l32 (plus 32 per
+  // block), logical chunk of dims (16i + 8g) [bf16] or element 2i + g [fp32].
+  constexpr int RB = D * int(sizeof(T));  // bytes per LDS row
+  int koff[kQRegs];
+#pragma unroll
+  for (int i = 0; i < kQRegs; ++i) {
+    if constexpr (kBF) {
+      const int lc = 2 * i + g;
+      koff[i] = l32 * RB + ((lc ^ Lds::k_swz(l32)) * 16);
+    } else {
+      const int e = 2 * i + g;
+      koff[i] = l32 * RB + (((e / 4) ^ Lds::k_swz(l32)) * 16) + (e % 4) * 4;
+    }
+  }
+  // V^T operand (bf16): for dim tile t, the lane's transpose-read address in
+  // 16-key chunk c, half hh is row 16c + 8hh + vrow, dims 32t + vdim .. +3.
+  const int vrow = 4 * g + ((lane & 15) >> 2);
+  const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int voff[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    const int dim = 32 * t + vdim;
+    voff[t] = vrow * RB + (((dim / 8) ^ Lds::v_swz(vrow)) * 16) + (dim % 8) * 2;
+  }
+
   f32x16 acc[D / 32];
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc[t][j] = 0.f;
+  for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
   float m2 = -INFINITY;  // running maximum, in log2 units (scaled)
   float lsum = 0.f;      // this lane half's share of the row sum
 
-  // ---- staging: global -> registers -> LDS
-  uint4 kreg[Lds::kKPerThread];
-  typename std::conditional<kBF, uint2, uint4>::type vreg[kBF ? 4 * Lds::kVPerThread : Lds::kVPerThread];
+  TileCursor ck, cv;  // next K tile to load, next V tile to load
+  ck.init(p.ranges, task.r0, task.r1);
+  cv = ck;
+  TileLoader<T, D, false> kld;
+  TileLoader<T, D, true> vld;
+  kld.init(rs, tid);
+  vld.init(rs, tid);
 
-  auto load_tile = [&](int32_t ks, int32_t nv) {
-#pragma unroll
-    for (int i = 0; i < Lds::kKPerThread; ++i) {
-      const int c = tid + i * kAttnThreads;
-      if (c < Lds::kKChunks) {
-        constexpr int cpr = D * int(sizeof(T)) / 16;  // chunks per row
-        const int r = c / cpr, cc = c - (c / cpr) * cpr;
-        const int32_t row = ks + min(r, nv - 1);
-        kreg[i] = *reinterpret_cast<const uint4*>(kg + row * rs + cc * (16 / int(sizeof(T))));
-      }
-    }
-    if constexpr (kBF) {
-#pragma unroll
-      for (int i = 0; i < Lds::kVPerThread; ++i) {
-        const int u = tid + i * kAttnThreads;
-        if (u < Lds::kVUnits) {
-          const int kgp = u & 15, dq = u >> 4;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int32_t row = ks + min(4 * kgp + r, nv - 1);
-            vreg[4 * i + r] = *reinterpret_cast<const uint2*>(vg + row * rs + 4 * dq);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < Lds::kVPerThread; ++i) {
-        const int c = tid + i * kAttnThreads;
-        if (c < Lds::kVUnits) {
-          constexpr int cpr = D * int(sizeof(T)) / 16;
-          const int r = c / cpr, cc = c - (c / cpr) * cpr;
-          const int32_t row = ks + min(r, nv - 1);
-          vreg[i] = *reinterpret_cast<const uint4*>(vg + row * rs + cc * 4);
-        }
-      }
-    }
-  };
+  // prologue: K_0 -> K slot 0, K_1 -> K slot 1, V_0 -> V slot 0; S_0
+  kld.issue(kg, rs, ck.ks, ck.nv(), smem, tid, wave);
+  vld.issue(vg, rs, cv.ks, cv.nv(), smem + 2 * TB, tid, wave);
+  int32_t nv_cur = cv.nv();
+  ck.advance(p.ranges);
+  cv.advance(p.ranges);
+  if (ntiles > 1) {
+    kld.issue(kg, rs, ck.ks, ck.nv(), smem + TB, tid, wave);
+    ck.advance(p.ranges);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  qk_tile<T, D>(sa, smem, qf, koff);
+  __syncthreads();  // step 0 overwrites K slot 0 with K_2
 
-  auto store_tile = [&](T* stage) {
-    T* ks_ = stage;
-    T* vs_ = stage + Lds::kKElems;
-#pragma unroll
-    for (int i = 0; i < Lds::kKPerThread; ++i) {
-      const int c = tid + i * kAttnThreads;
-      if (c < Lds::kKChunks) {
-        constexpr int cpr = D * int(sizeof(T)) / 16;
-        const int r = c / cpr, cc = c - (c / cpr) * cpr;
-        *reinterpret_cast<uint4*>(ks_ + r * Lds::kKStride + cc * (16 / int(sizeof(T)))) = kreg[i];
-      }
+  // One pipeline step: softmax + PV of tile i (scores in s_cur) overlapped
+  // with QK^T of tile i+1 into s_next.  PAR = i & 1 (compile time).
+  auto step = [&](int32_t i, auto par, f32x16(&s_cur)[2], f32x16(&s_next)[2]) {
+    constexpr int PAR = decltype(par)::value;
+    char* const k_next = smem + (PAR ? 0 : TB);            // holds K_{i+1}
+    char* const v_cur = smem + 2 * TB + (PAR ? TB : 0);    // holds V_i
+    const bool has_k = i + 2 < ntiles;
+    const bool has_v = i + 1 < ntiles;
+    const int32_t nv_next = has_v ? cv.nv() : 0;
+    if (has_k) {  // K_{i+2} replaces K_i
+      kld.issue(kg, rs, ck.ks, ck.nv(), smem + (PAR ? TB : 0), tid, wave);
+      ck.advance(p.ranges);
     }
-    if constexpr (kBF) {
-#pragma unroll
-      for (int i = 0; i < Lds::kVPerThread; ++i) {
-        const int u = tid + i * kAttnThreads;
-        if (u < Lds::kVUnits) {
-          const int kgp = u & 15, dq = u >> 4;
-          // key group kgp of 4 keys -> position group: chunk kgp/4 of 16
-          // positions, in-chunk group order (0, 2, 1, 3) so that lane half g
-          // finds keys {4g..4g+3, 8+4g..8+4g+3} at positions 8g..8g+7.
-          const int sub = kgp & 3;
-          const int pg = (sub == 1) ? 2 : (sub == 2) ? 1 : sub;
-          const int pos = (kgp >> 2) * 16 + pg * 4;
-          const uint2 r0 = vreg[4 * i + 0], r1 = vreg[4 * i + 1], r2 = vreg[4 * i + 2], r3 = vreg[4 * i + 3];
-          // 4x4 transpose of 16-bit values: dim e gets keys 0..3 of the group.
-          auto lo2 = [](uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); };
-          auto hi2 = [](uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); };
-          const uint2 o0 = make_uint2(lo2(r0.x, r1.x), lo2(r2.x, r3.x));
-          const uint2 o1 = make_uint2(hi2(r0.x, r1.x), hi2(r2.x, r3.x));
-          const uint2 o2 = make_uint2(lo2(r0.y, r1.y), lo2(r2.y, r3.y));
-          const uint2 o3 = make_uint2(hi2(r0.y, r1.y), hi2(r2.y, r3.y));
-          T* base = vs_ + (4 * dq) * Lds::kVStride + pos;
-          *reinterpret_cast<uint2*>(base + 0 * Lds::kVStride) = o0;
-          *reinterpret_cast<uint2*>(base + 1 * Lds::kVStride) = o1;
-          *reinterpret_cast<uint2*>(base + 2 * Lds::kVStride) = o2;
-          *reinterpret_cast<uint2*>(base + 3 * Lds::kVStride) = o3;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < Lds::kVPerThread; ++i) {
-        const int c = tid + i * kAttnThreads;
-        if (c < Lds::kVUnits) {
-          constexpr int cpr = D * int(sizeof(T)) / 16;
-          const int r = c / cpr, cc = c - (c / cpr) * cpr;
-          *reinterpret_cast<uint4*>(vs_ + r * Lds::kVStride + cc * 4) = vreg[i];
-        }
-      }
+    if (has_v) {  // V_{i+1} replaces V_{i-1}
+      vld.issue(vg, rs, cv.ks, nv_next, smem + 2 * TB + (PAR ? 0 : TB), tid, wave);
+      cv.advance(p.ranges);
     }
-  };
 
-  auto compute = [&](const T* stage, int32_t nv) {
-    const T* ks_ = stage;
-    const T* vs_ = stage + Lds::kKElems;
-    f32x16 s[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) s[mb][j] = 0.f;
-      const T* krow = ks_ + (mb * 32 + l32) * Lds::kKStride;
-#pragma unroll
-      for (int i = 0; i < kQRegs; ++i) {
-        if constexpr (kBF) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * i + 8 * g);
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i], s[mb], 0, 0, 0);
-        } else {
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * i + g], qf[i], s[mb], 0, 0, 0);
-        }
-      }
-    }
-    if (nv < kKT) {  // ragged tail of a key range (uniform)
+    if (nv_cur < kKT) {  // ragged tail of a key range (uniform)
+      const int lim = nv_cur - 4 * g;  // key 8*(j/4) + 4g + j%4 of block mb is valid iff its offset < lim
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          if (mb * 32 + 8 * (j >> 2) + 4 * g + (j & 3) >= nv) s[mb][j] = -INFINITY;
+          if (mb * 32 + 8 * (j >> 2) + (j & 3) >= lim) s_cur[mb][j] = -INFINITY;
     }
-    float mx = s[0][0];
+    float mx = s_cur[0][0];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[mb][j]);
-    mx = fmaxf(mx, wave_other_half(mx));
-    const float mt = mx * p.scale_log2;
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s_cur[mb][j]);
+    mx = pair_max(mx);
+    const float mt = mx * c2;
     const bool need = mt > m2 + 8.0f;
     if (__ballot(need)) {
       const float mnew = need ? mt : m2;
@@ -395,21 +471,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
       m2 = mnew;
       lsum *= alpha;
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[t][j] *= alpha;
+      for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
     }
+
+    // exponentials of tile i (VALU) interleave with QK^T of tile i+1 (MFMA)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) s[mb][j] = __builtin_amdgcn_exp2f(fmaf(s[mb][j], p.scale_log2, -m2));
+      for (int j = 0; j < 16; ++j) s_cur[mb][j] = __builtin_amdgcn_exp2f(fmaf(s_cur[mb][j], c2, -m2));
+    qk_tile<T, D>(s_next, k_next, qf, koff);
 
     if constexpr (kBF) {
       bf16x8 pb[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[c][e] = __bf16(s[c >> 1][(c & 1) * 8 + e]);
+        for (int e = 0; e < 8; ++e) pb[c][e] = __bf16(s_cur[c >> 1][(c & 1) * 8 + e]);
       typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
       const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
 #pragma unroll
@@ -421,10 +498,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
         }
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) {
-        const T* vrow = vs_ + (t * 32 + l32) * Lds::kVStride;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + 16 * c + 8 * g);
+          const char* a0 = v_cur + voff[t] + (16 * c) * RB;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * RB));
+          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[t], 0, 0, 0);
         }
       }
@@ -432,7 +511,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) lsum += s[mb][j];
+        for (int j = 0; j < 16; ++j) lsum += s_cur[mb][j];
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -440,68 +519,55 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int key = mb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs_[key * Lds::kVStride + t * 32 + l32], s[mb][j],
-                                                          acc[t], 0, 0, 0);
+            const int dim = 32 * t + l32;
+            const float vv = *reinterpret_cast<const float*>(v_cur + key * RB +
+                                                             (((dim / 4) ^ Lds::v_swz(key)) * 16) + (dim % 4) * 4);
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, s_cur[mb][j], acc[t], 0, 0, 0);
           }
     }
-  };
 
-  // ---- walk the key ranges in 64-key tiles
-  int32_t ri = task.r0;
-  ug::Range cur = p.ranges[ri];
-  int32_t ks = cur.k0;
-  auto advance = [&]() {
-    ks += kKT;
-    if (ks >= cur.k1) {
-      ++ri;
-      if (ri < task.r1) {
-        cur = p.ranges[ri];
-        ks = cur.k0;
-      }
-    }
-  };
-
-  int32_t nv = min(kKT, cur.k1 - ks);
-  load_tile(ks, nv);
-  store_tile(smem);
-  __syncthreads();
-  advance();
-  for (int it = 0;; ++it) {
-    const bool has_next = ri < task.r1;
-    int32_t nv_next = 0;
-    if (has_next) {
-      nv_next = min(kKT, cur.k1 - ks);
-      load_tile(ks, nv_next);
-    }
-    if (wave_active) compute(smem + (it & 1) * Lds::kStageElems, nv);
-    if (!has_next) break;
-    store_tile(smem + ((it + 1) & 1) * Lds::kStageElems);
+    nv_cur = nv_next;
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's direct-to-LDS loads have landed
     __syncthreads();
-    nv = nv_next;
-    advance();
+  };
+
+  for (int32_t i = 0; i < ntiles; i += 2) {
+    step(i, std::integral_constant<int, 0>{}, sa, sb);
+    if (i + 1 >= ntiles) break;
+    step(i + 1, std::integral_constant<int, 1>{}, sb, sa);
   }
 
-  // ---- epilogue: combine the two lane halves' row sums, normalise, store
-  const float ltot = lsum + wave_other_half(lsum);
-  if (!wave_active || !qvalid) return;
-  const float inv = 1.0f / ltot;
-  T* orow = og + qrow * rs;
+  // ---- epilogue: combine the lane halves' row sums, normalise, and write
+  // the wave's 32 x D output block through LDS (swizzled rows) as full rows.
+  const float inv = 1.0f / pair_sum(lsum);
+  char* const ost = smem + wave * 32 * RB;
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const int d0 = t * 32 + 8 * q4 + 4 * g;
+      const int d0 = t * 32 + 8 * q4 + 4 * g;  // 4 consecutive dims
+      char* dst = ost + l32 * RB + (((d0 / Lds::kEl16) ^ Lds::k_swz(l32)) * 16) + (d0 % Lds::kEl16) * int(sizeof(T));
       if constexpr (kBF) {
         bf16x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = __bf16(acc[t][4 * q4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + d0) = w;
+        *reinterpret_cast<bf16x4*>(dst) = w;
       } else {
-        float4 w = make_float4(acc[t][4 * q4 + 0] * inv, acc[t][4 * q4 + 1] * inv, acc[t][4 * q4 + 2] * inv,
-                               acc[t][4 * q4 + 3] * inv);
-        *reinterpret_cast<float4*>(orow + d0) = w;
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[t][4 * q4 + 0] * inv, acc[t][4 * q4 + 1] * inv,
+                                                      acc[t][4 * q4 + 2] * inv, acc[t][4 * q4 + 3] * inv);
       }
     }
+  // each wave reads back only its own block: LDS operations of one wave
+  // complete in order, so no barrier is needed between the write and read.
+  constexpr int rows_per_pass = 64 / Lds::kChunks;
+#pragma unroll
+  for (int pass = 0; pass < 32 / rows_per_pass; ++pass) {
+    const int r = pass * rows_per_pass + lane / Lds::kChunks;
+    const int cc = lane % Lds::kChunks;
+    const uint4 val = *reinterpret_cast<const uint4*>(ost + r * RB + ((cc ^ Lds::k_swz(r)) * 16));
+    const int32_t row = task.q0 + wave * 32 + r;
+    if (row < task.q1) *reinterpret_cast<uint4*>(og + row * rs + cc * Lds::kEl16) = val;
+  }
 }
 
 // ---------------------------------------------------------------------------
