@@ -415,10 +415,43 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
   kld.init(rs, tid);
   vld.init(rs, tid);
 
+  // Scores of a freshly computed tile: mask a ragged tail (rare, uniform
+  // branch) and return the tile maximum (both lane halves agree).
+  auto mask_tail = [&](f32x16(&s)[2], int32_t nv) {
+    const int lim = nv - 4 * g;  // key 8*(j/4) + 4g + j%4 of block mb is valid iff its offset < lim
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (mb * 32 + 8 * (j >> 2) + (j & 3) >= lim) s[mb][j] = -INFINITY;
+  };
+  auto tile_max = [&](const f32x16(&s)[2]) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[mb][j]);
+    return pair_max(mx);
+  };
+  // Move the running maximum when the new tile's maximum exceeds it by more
+  // than 2^8 (log2 units), rescaling what has been accumulated so far.
+  auto update_max = [&](float mx, bool valid) {
+    const float mt = mx * c2;
+    const bool need = valid && mt > m2 + 8.0f;
+    if (__ballot(need)) {
+      const float mnew = need ? mt : m2;
+      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+      m2 = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+    }
+  };
+
   // prologue: K_0 -> K slot 0, K_1 -> K slot 1, V_0 -> V slot 0; S_0
   kld.issue(kg, rs, ck.ks, ck.nv(), smem, tid, wave);
   vld.issue(vg, rs, cv.ks, cv.nv(), smem + 2 * TB, tid, wave);
-  int32_t nv_cur = cv.nv();
+  const int32_t nv_cur = cv.nv();
   ck.advance(p.ranges);
   cv.advance(p.ranges);
   if (ntiles > 1) {
@@ -429,17 +462,23 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
   __syncthreads();
   f32x16 sa[2], sb[2];
   qk_tile<T, D>(sa, smem, qf, koff);
+  if (nv_cur < kKT) mask_tail(sa, nv_cur);
+  update_max(tile_max(sa), true);
   __syncthreads();  // step 0 overwrites K slot 0 with K_2
 
-  // One pipeline step: softmax + PV of tile i (scores in s_cur) overlapped
-  // with QK^T of tile i+1 into s_next.  PAR = i & 1 (compile time).
+  // One pipeline step on tile i, whose scores s_cur are masked and whose
+  // maximum is already folded into m2:
+  //   [A] exponentials of tile i (VALU)  ||  QK^T of tile i+1 (MFMA)
+  //   [B] PV of tile i (MFMA)            ||  maximum of tile i+1 (VALU)
+  // then the rare paths (ragged tail of tile i+1, moving the maximum).
+  // PAR = i & 1 selects the ring slots at compile time.
   auto step = [&](int32_t i, auto par, f32x16(&s_cur)[2], f32x16(&s_next)[2]) {
     constexpr int PAR = decltype(par)::value;
     char* const k_next = smem + (PAR ? 0 : TB);            // holds K_{i+1}
     char* const v_cur = smem + 2 * TB + (PAR ? TB : 0);    // holds V_i
     const bool has_k = i + 2 < ntiles;
     const bool has_v = i + 1 < ntiles;
-    const int32_t nv_next = has_v ? cv.nv() : 0;
+    const int32_t nv_next = has_v ? cv.nv() : kKT;
     if (has_k) {  // K_{i+2} replaces K_i
       kld.issue(kg, rs, ck.ks, ck.nv(), smem + (PAR ? TB : 0), tid, wave);
       ck.advance(p.ranges);
@@ -449,57 +488,34 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
       cv.advance(p.ranges);
     }
 
-    if (nv_cur < kKT) {  // ragged tail of a key range (uniform)
-      const int lim = nv_cur - 4 * g;  // key 8*(j/4) + 4g + j%4 of block mb is valid iff its offset < lim
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (mb * 32 + 8 * (j >> 2) + (j & 3) >= lim) s_cur[mb][j] = -INFINITY;
-    }
-    float mx = s_cur[0][0];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s_cur[mb][j]);
-    mx = pair_max(mx);
-    const float mt = mx * c2;
-    const bool need = mt > m2 + 8.0f;
-    if (__ballot(need)) {
-      const float mnew = need ? mt : m2;
-      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-      m2 = mnew;
-      lsum *= alpha;
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
-    }
-
-    // exponentials of tile i (VALU) interleave with QK^T of tile i+1 (MFMA)
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) s_cur[mb][j] = __builtin_amdgcn_exp2f(fmaf(s_cur[mb][j], c2, -m2));
-    qk_tile<T, D>(s_next, k_next, qf, koff);
-
     if constexpr (kBF) {
+      // [A]
       bf16x8 pb[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[c][e] = __bf16(s_cur[c >> 1][(c & 1) * 8 + e]);
       typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
       const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pb[c][e] = __bf16(__builtin_amdgcn_exp2f(fmaf(s_cur[c >> 1][(c & 1) * 8 + e], c2, -m2)));
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const bf16x2 pr = {pb[c][e], pb[c][e + 1]};
           lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
         }
+      }
+      qk_tile<T, D>(s_next, k_next, qf, koff);
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
+      for (int k = 0; k < 2 * (D / 16); ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      }
+      // [B]
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
           const char* a0 = v_cur + voff[t] + (16 * c) * RB;
           const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
           const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * RB));
@@ -507,11 +523,29 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
           acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[t], 0, 0, 0);
         }
       }
+      const float mx_next = tile_max(s_next);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);  // DS read (run ahead)
+#pragma unroll
+      for (int k = 0; k < 4 * (D / 32); ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);  // VALU
+      }
+      if (nv_next < kKT) {
+        mask_tail(s_next, nv_next);
+        update_max(tile_max(s_next), has_v);
+      } else {
+        update_max(mx_next, has_v);
+      }
     } else {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) lsum += s_cur[mb][j];
+        for (int j = 0; j < 16; ++j) {
+          s_cur[mb][j] = __builtin_amdgcn_exp2f(fmaf(s_cur[mb][j], c2, -m2));
+          lsum += s_cur[mb][j];
+        }
+      qk_tile<T, D>(s_next, k_next, qf, koff);
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -524,9 +558,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
                                                              (((dim / 4) ^ Lds::v_swz(key)) * 16) + (dim % 4) * 4);
             acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, s_cur[mb][j], acc[t], 0, 0, 0);
           }
+      if (nv_next < kKT) mask_tail(s_next, nv_next);
+      update_max(tile_max(s_next), has_v);
     }
 
-    nv_cur = nv_next;
     __builtin_amdgcn_s_waitcnt(0);  // this thread's direct-to-LDS loads have landed
     __syncthreads();
   };
