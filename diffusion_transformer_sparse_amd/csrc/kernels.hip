@@ -28,44 +28,38 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
 // Row gather: dst row j <- src row map(j), whole token rows (all heads) at a
-// time, 16-byte vectors.  Rows outside [T, T+N) (text, LR) copy in place;
-// HR row T+i copies from T + table[i].  With table = perm this is the
-// window-first permutation, with table = inverse it is the unpermutation.
-// Pure HBM streaming: every byte is read once and written once.
+// time.  Rows outside [T, T+N) (text, LR) copy in place; HR row T+i copies
+// from T + table[i].  With table = perm this is the window-first
+// permutation, with table = inverse it is the unpermutation.  Pure HBM
+// streaming: every byte is read once and written once, so the accesses are
+// non-temporal 16-byte vectors; each thread owns one 16-byte column of
+// kGatherRows consecutive rows and has all of them in flight at once.
 // ---------------------------------------------------------------------------
-constexpr int kGatherThreads = 256;
-constexpr int kGatherRows = 8;     // token rows per workgroup
-constexpr int kGatherUnroll = 4;   // 16-B loads in flight per thread
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kGatherRows = 4;  // token rows per workgroup
 
-__global__ __launch_bounds__(kGatherThreads) void row_gather_kernel(const uint4* __restrict__ src,
-                                                                     uint4* __restrict__ dst, int32_t L, int32_t T,
-                                                                     int32_t N, int32_t units,
-                                                                     const int32_t* __restrict__ table) {
+__global__ __launch_bounds__(1024) void row_gather_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                          int32_t L, int32_t T, int32_t N, int32_t units,
+                                                          const int32_t* __restrict__ table) {
   const int64_t batch_units = int64_t(L) * units;
   src += blockIdx.y * batch_units;
   dst += blockIdx.y * batch_units;
   const int32_t row0 = blockIdx.x * kGatherRows;
-  const int32_t nrows = min(kGatherRows, L - row0);
-  const int32_t total = nrows * units;
-  for (int32_t base = threadIdx.x; base < total; base += kGatherThreads * kGatherUnroll) {
-    uint4 v[kGatherUnroll];
-    int64_t doff[kGatherUnroll];
+  for (int32_t c = threadIdx.x; c < units; c += blockDim.x) {
+    u32x4 v[kGatherRows];
 #pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u) {
-      const int32_t f = base + u * kGatherThreads;
-      doff[u] = -1;
-      if (f < total) {
-        const int32_t r = f / units;
-        const int32_t c = f - r * units;
-        const int32_t j = row0 + r;
+    for (int r = 0; r < kGatherRows; ++r) {
+      const int32_t j = row0 + r;
+      if (j < L) {
         const int32_t s = (j >= T && j < T + N) ? T + table[j - T] : j;
-        v[u] = src[int64_t(s) * units + c];
-        doff[u] = int64_t(j) * units + c;
+        v[r] = __builtin_nontemporal_load(src + int64_t(s) * units + c);
       }
     }
 #pragma unroll
-    for (int u = 0; u < kGatherUnroll; ++u)
-      if (doff[u] >= 0) dst[doff[u]] = v[u];
+    for (int r = 0; r < kGatherRows; ++r) {
+      const int32_t j = row0 + r;
+      if (j < L) __builtin_nontemporal_store(v[r], dst + int64_t(j) * units + c);
+    }
   }
 }
 
@@ -75,80 +69,92 @@ __global__ __launch_bounds__(kGatherThreads) void row_gather_kernel(const uint4*
 // T+N+i holds LR token (m, n) = (i / w, i % w) at position (rho*m, rho*n).
 // Dims [0, D/2) turn by the row position, [D/2, D) by the column position;
 // pair (2k, 2k+1) of a half turns by pos * omega_k, (cos, sin) from the
-// plan's table cs[pos][k].  Each thread owns one 16-byte vector of one head
-// row in both Q and K.
+// plan's table cs[pos][k].  Each thread owns one 16-byte column (part of one
+// head) of kRopeRows consecutive rows in both Q and K, all loads in flight at
+// once; every byte is read and written once, with non-temporal accesses.
 // ---------------------------------------------------------------------------
-constexpr int kRopeThreads = 256;
+constexpr int kRopeRows = 4;  // token rows per workgroup
 
 template <typename T>
-__global__ __launch_bounds__(kRopeThreads) void rope2d_kernel(T* __restrict__ q, T* __restrict__ k, int32_t L,
-                                                              int32_t T0, int32_t N, int32_t W, int32_t lr_w,
-                                                              int32_t rho, int32_t heads, int32_t D,
-                                                              const int32_t* __restrict__ perm,
-                                                              const float2* __restrict__ cs) {
-  constexpr int E = 16 / sizeof(T);  // elements per thread (8 bf16 or 4 fp32)
+__global__ __launch_bounds__(1024) void rope2d_kernel(T* __restrict__ q, T* __restrict__ k, int32_t L, int32_t T0,
+                                                      int32_t N, int32_t W, int32_t lr_w, int32_t rho, int32_t heads,
+                                                      int32_t D, const int32_t* __restrict__ perm,
+                                                      const float2* __restrict__ cs) {
+  constexpr int E = 16 / sizeof(T);  // elements per 16-byte vector (8 bf16 or 4 fp32)
   const int32_t units_per_head = D / E;
   const int32_t units = heads * units_per_head;
-  const int64_t rows = int64_t(L - T0);  // HR + LR rows
-  const int64_t f = int64_t(blockIdx.x) * kRopeThreads + threadIdx.x;
-  if (f >= rows * units) return;
-  const int32_t rr = int32_t(f / units);
-  const int32_t c = int32_t(f - int64_t(rr) * units);
-  const int32_t j = T0 + rr;
-  int32_t pr, pc;
-  if (rr < N) {
-    const int32_t idx = perm[rr];
-    pr = idx / W;
-    pc = idx - pr * W;
-  } else {
-    const int32_t i = rr - N;
-    const int32_t m = i / lr_w;
-    pr = rho * m;
-    pc = rho * (i - m * lr_w);
-  }
-  const int32_t e0 = (c % units_per_head) * E;  // first dim of this vector
-  const int32_t half = D / 2;
-  const int32_t pos = e0 < half ? pr : pc;
-  const int32_t k0 = (e0 < half ? e0 : e0 - half) / 2;  // first pair index
-  const float2* tab = cs + int64_t(pos) * (D / 4) + k0;
-  const int64_t off = (int64_t(blockIdx.y) * L + j) * units + c;  // in 16-B units
-  uint4* qv = reinterpret_cast<uint4*>(q) + off;
-  uint4* kv = reinterpret_cast<uint4*>(k) + off;
-  uint4 qa = *qv, ka = *kv;
-  if constexpr (std::is_same<T, float>::value) {
-    const float2 t0 = tab[0], t1 = tab[1];
-    float* x = reinterpret_cast<float*>(&qa);
-    float* y = reinterpret_cast<float*>(&ka);
-    const float2 t[2] = {t0, t1};
+  const int32_t rows = L - T0;  // HR + LR rows
+  const int32_t rr0 = blockIdx.x * kRopeRows;
+  const int64_t boff = int64_t(blockIdx.y) * L * units;
+  u32x4* const qv = reinterpret_cast<u32x4*>(q) + boff;
+  u32x4* const kv = reinterpret_cast<u32x4*>(k) + boff;
+  // (row, column) positions of this workgroup's rows
+  int32_t pr[kRopeRows], pc[kRopeRows];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const float a = x[2 * p], b = x[2 * p + 1];
-      x[2 * p] = a * t[p].x - b * t[p].y;
-      x[2 * p + 1] = a * t[p].y + b * t[p].x;
-      const float a2 = y[2 * p], b2 = y[2 * p + 1];
-      y[2 * p] = a2 * t[p].x - b2 * t[p].y;
-      y[2 * p + 1] = a2 * t[p].y + b2 * t[p].x;
+  for (int r = 0; r < kRopeRows; ++r) {
+    const int32_t rr = min(rr0 + r, rows - 1);
+    if (rr < N) {
+      const int32_t idx = perm[rr];
+      pr[r] = idx / W;
+      pc[r] = idx - pr[r] * W;
+    } else {
+      const int32_t i = rr - N;
+      const int32_t m = i / lr_w;
+      pr[r] = rho * m;
+      pc[r] = rho * (i - m * lr_w);
     }
-  } else {
-    float2 t[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) t[p] = tab[p];
-    bf16x8 x = *reinterpret_cast<bf16x8*>(&qa);
-    bf16x8 y = *reinterpret_cast<bf16x8*>(&ka);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float a = float(x[2 * p]), b = float(x[2 * p + 1]);
-      x[2 * p] = __bf16(a * t[p].x - b * t[p].y);
-      x[2 * p + 1] = __bf16(a * t[p].y + b * t[p].x);
-      const float a2 = float(y[2 * p]), b2 = float(y[2 * p + 1]);
-      y[2 * p] = __bf16(a2 * t[p].x - b2 * t[p].y);
-      y[2 * p + 1] = __bf16(a2 * t[p].y + b2 * t[p].x);
-    }
-    qa = *reinterpret_cast<uint4*>(&x);
-    ka = *reinterpret_cast<uint4*>(&y);
   }
-  *qv = qa;
-  *kv = ka;
+  for (int32_t c = threadIdx.x; c < units; c += blockDim.x) {
+    const int32_t e0 = (c % units_per_head) * E;  // first dim of this vector
+    const bool col = e0 >= D / 2;
+    const int32_t k0 = (col ? e0 - D / 2 : e0) / 2;  // first pair index
+    u32x4 qa[kRopeRows], ka[kRopeRows];
+#pragma unroll
+    for (int r = 0; r < kRopeRows; ++r) {
+      if (rr0 + r < rows) {
+        const int64_t off = int64_t(T0 + rr0 + r) * units + c;
+        qa[r] = __builtin_nontemporal_load(qv + off);
+        ka[r] = __builtin_nontemporal_load(kv + off);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRopeRows; ++r) {
+      if (rr0 + r >= rows) continue;
+      const float2* tab = cs + int64_t(col ? pc[r] : pr[r]) * (D / 4) + k0;
+      if constexpr (std::is_same<T, float>::value) {
+        float* x = reinterpret_cast<float*>(&qa[r]);
+        float* y = reinterpret_cast<float*>(&ka[r]);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const float2 t = tab[p];
+          const float a = x[2 * p], b = x[2 * p + 1];
+          x[2 * p] = a * t.x - b * t.y;
+          x[2 * p + 1] = a * t.y + b * t.x;
+          const float a2 = y[2 * p], b2 = y[2 * p + 1];
+          y[2 * p] = a2 * t.x - b2 * t.y;
+          y[2 * p + 1] = a2 * t.y + b2 * t.x;
+        }
+      } else {
+        bf16x8 x = *reinterpret_cast<bf16x8*>(&qa[r]);
+        bf16x8 y = *reinterpret_cast<bf16x8*>(&ka[r]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float2 t = tab[p];
+          const float a = float(x[2 * p]), b = float(x[2 * p + 1]);
+          x[2 * p] = __bf16(a * t.x - b * t.y);
+          x[2 * p + 1] = __bf16(a * t.y + b * t.x);
+          const float a2 = float(y[2 * p]), b2 = float(y[2 * p + 1]);
+          y[2 * p] = __bf16(a2 * t.x - b2 * t.y);
+          y[2 * p + 1] = __bf16(a2 * t.y + b2 * t.x);
+        }
+        qa[r] = *reinterpret_cast<u32x4*>(&x);
+        ka[r] = *reinterpret_cast<u32x4*>(&y);
+      }
+      const int64_t off = int64_t(T0 + rr0 + r) * units + c;
+      __builtin_nontemporal_store(qa[r], qv + off);
+      __builtin_nontemporal_store(ka[r], kv + off);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -653,8 +659,9 @@ ug_status gather(ug_plan_t p, const void* src, void* dst, const int32_t* table, 
     return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": current device is not the plan's device");
   const int32_t units = int32_t(int64_t(p->d.heads) * p->d.head_dim * (p->d.dtype == UG_BF16 ? 2 : 4) / 16);
   const dim3 grid(unsigned((p->L + kGatherRows - 1) / kGatherRows), unsigned(p->d.batch));
-  hipLaunchKernelGGL(row_gather_kernel, grid, dim3(kGatherThreads), 0, s, static_cast<const uint4*>(src),
-                     static_cast<uint4*>(dst), int32_t(p->L), int32_t(p->T), int32_t(p->N), units, table);
+  const unsigned threads = unsigned(std::min<int64_t>(1024, (int64_t(units) + 63) / 64 * 64));
+  hipLaunchKernelGGL(row_gather_kernel, grid, dim3(threads), 0, s, static_cast<const u32x4*>(src),
+                     static_cast<u32x4*>(dst), int32_t(p->L), int32_t(p->T), int32_t(p->N), units, table);
   return launch_status(fn);
 }
 
@@ -690,17 +697,17 @@ ug_status ug_rope2d(ug_plan_t p, void* q_perm, void* k_perm, void* stream) {
   if (rows == 0) return UG_OK;
   const int E = p->d.dtype == UG_BF16 ? 8 : 4;
   const int64_t units = int64_t(p->d.heads) * p->d.head_dim / E;
-  const int64_t total = rows * units;
-  const dim3 grid(unsigned((total + kRopeThreads - 1) / kRopeThreads), unsigned(p->d.batch));
+  const dim3 grid(unsigned((rows + kRopeRows - 1) / kRopeRows), unsigned(p->d.batch));
+  const unsigned threads = unsigned(std::min<int64_t>(1024, (units + 63) / 64 * 64));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float2* cs = reinterpret_cast<const float2*>(p->d_rope);
   const int32_t lr_w = std::max(p->d.lr_w, 1);
   if (p->d.dtype == UG_BF16)
-    hipLaunchKernelGGL(rope2d_kernel<__bf16>, grid, dim3(kRopeThreads), 0, s, static_cast<__bf16*>(q_perm),
+    hipLaunchKernelGGL(rope2d_kernel<__bf16>, grid, dim3(threads), 0, s, static_cast<__bf16*>(q_perm),
                        static_cast<__bf16*>(k_perm), int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w,
                        p->d.rho, p->d.heads, p->d.head_dim, p->d_perm, cs);
   else
-    hipLaunchKernelGGL(rope2d_kernel<float>, grid, dim3(kRopeThreads), 0, s, static_cast<float*>(q_perm),
+    hipLaunchKernelGGL(rope2d_kernel<float>, grid, dim3(threads), 0, s, static_cast<float*>(q_perm),
                        static_cast<float*>(k_perm), int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w,
                        p->d.rho, p->d.heads, p->d.head_dim, p->d_perm, cs);
   return launch_status("ug_rope2d");
