@@ -4,8 +4,11 @@
 A step is the whole hot path over one batch of synthetic input already
 resident in HBM: window-first permutation of Q, K and V, 2D axial RoPE on Q
 and K, the composite-masked attention forward, and the inverse permutation of
-O.  The plan (host tables, built once per resolution and reused by every
-layer and denoising step) is built before the timed region.
+O, run as three launches (permutation+RoPE of Q and K fused, permutation of
+V, attention with the inverse permutation in its epilogue).  The same path as
+one call per step is timed too and reported under "unfused".  The plan (host
+tables, built once per resolution and reused by every layer and denoising
+step) is built before the timed region.
 
 Prints ONE JSON line.  `value` is effective TFLOP/s of the whole step:
 4 * D * (allowed query-key pairs) * heads / step time, i.e. only unmasked
@@ -110,10 +113,27 @@ def main():
 
     q, k, v = (to_dev(WL.tensor_storage(w, t)) for t in (WL.Q, WL.K, WL.V))
     out = torch.empty_like(q)
-    layer = U.Layer(plan, dev)
+    layer = U.Layer(plan, dev)  # buffers for the permuted Q, K, V and O
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
+    # The timed step: window-first permutation + RoPE of Q and K in one pass,
+    # permutation of V, attention writing O in raster order (the inverse
+    # permutation folded into its epilogue).
+    def step_fused(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        U.ug_permute_rope(plan, q, k, layer.qp, layer.kp)
+        if ev is not None:
+            ev[1].record(stream)
+        U.ug_permute(plan, v, layer.vp)
+        if ev is not None:
+            ev[2].record(stream)
+        U.ug_attn_fwd_raster(plan, layer.qp, layer.kp, layer.vp, out)
+        if ev is not None:
+            ev[3].record(stream)
+
+    # The same path as one call per step: permute x3, RoPE, attention, unpermute.
+    def step_unfused(ev=None):
         if ev is not None:
             ev[0].record(stream)
         U.ug_permute(plan, q, layer.qp)
@@ -131,22 +151,26 @@ def main():
         if ev is not None:
             ev[4].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall / args.steps * 1e3
+    def timed(step, n_events, steps, warmup):
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_events)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) / steps * 1e3
+        avg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in events) / len(events)
+        return wall_ms, avg
 
-    def avg(a, b):
-        return sum(e[a].elapsed_time(e[b]) for e in events) / len(events)
+    layer.op = torch.empty_like(q)
+    ms_step, avg = timed(step_fused, 4, args.steps, args.warmup)
+    ms_prq, ms_pv, ms_attn = avg(0, 1), avg(1, 2), avg(2, 3)
+    ums_step, uavg = timed(step_unfused, 5, max(5, args.steps // 2), 2)
+    ums_perm3, ums_rope, ums_attn, ums_unperm = uavg(0, 1), uavg(1, 2), uavg(2, 3), uavg(3, 4)
 
-    ms_perm3, ms_rope, ms_attn, ms_unperm = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
     esize = 2 if w.dtype == "bf16" else 4
     tbytes = w.batch * w.seq_len * w.heads * w.head_dim * esize
     rope_bytes = 2 * 2 * w.batch * (w.n_hr + w.n_lr) * w.heads * w.head_dim * esize
@@ -157,6 +181,9 @@ def main():
 
     def gbs(nbytes, ms):
         return nbytes / (ms * 1e-3) / 1e9
+
+    def hbm(nbytes, ms):
+        return {"ms": round(ms, 4), "gbs": round(gbs(nbytes, ms), 1), "frac_hbm": round(gbs(nbytes, ms) / PEAK_HBM_GBS, 4)}
 
     res = {
         "metric": "effective attn TFLOP/s + ms/layer at 4K (65,536 HR tok), % of bf16 MFMA peak",
@@ -174,19 +201,24 @@ def main():
         "config": {"workload": w.name, "hr_grid": [w.hr_h, w.hr_w], "lr_grid": [w.lr_h, w.lr_w],
                    "n_text": w.n_text, "heads": w.heads, "head_dim": w.head_dim, "window": w.window,
                    "radius": w.radius, "rho": w.rho, "batch": w.batch, "seq_len": w.seq_len,
-                   "pairs_per_head": info["pairs_per_head"], "eff_flop_per_step": flops},
+                   "pairs_per_head": info["pairs_per_head"], "eff_flop_per_step": flops,
+                   "step": "ug_permute_rope(Q,K) + ug_permute(V) + ug_attn_fwd_raster"},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tflops, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
                      "traffic": traffic},
         "kernels": {
-            "attn_fwd": {"ms": round(ms_attn, 4), "eff_tflops": round(attn_tflops, 2),
-                         "frac_peak": round(attn_tflops / peak, 4)},
-            "permute_qkv": {"ms": round(ms_perm3, 4), "gbs": round(gbs(3 * 2 * tbytes, ms_perm3), 1),
-                            "frac_hbm": round(gbs(3 * 2 * tbytes, ms_perm3) / PEAK_HBM_GBS, 4)},
-            "rope2d_qk": {"ms": round(ms_rope, 4), "gbs": round(gbs(rope_bytes, ms_rope), 1),
-                          "frac_hbm": round(gbs(rope_bytes, ms_rope) / PEAK_HBM_GBS, 4)},
-            "unpermute_o": {"ms": round(ms_unperm, 4), "gbs": round(gbs(2 * tbytes, ms_unperm), 1),
-                            "frac_hbm": round(gbs(2 * tbytes, ms_unperm) / PEAK_HBM_GBS, 4)},
+            "attn_fwd_raster": {"ms": round(ms_attn, 4), "eff_tflops": round(attn_tflops, 2),
+                                "frac_peak": round(attn_tflops / peak, 4)},
+            "permute_rope_qk": hbm(2 * 2 * tbytes, ms_prq),
+            "permute_v": hbm(2 * tbytes, ms_pv),
+        },
+        "unfused": {
+            "ms_per_step": round(ums_step, 4),
+            "value": round(flops / (ums_step * 1e-3) / 1e12, 2),
+            "attn_fwd": {"ms": round(ums_attn, 4), "eff_tflops": round(flops / (ums_attn * 1e-3) / 1e12, 2)},
+            "permute_qkv": hbm(3 * 2 * tbytes, ums_perm3),
+            "rope2d_qk": hbm(rope_bytes, ums_rope),
+            "unpermute_o": hbm(2 * tbytes, ums_unperm),
         },
         "plan_build_s": round(t_plan, 4),
         "kernel_sha": kernel_hash(),

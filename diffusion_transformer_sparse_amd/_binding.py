@@ -20,7 +20,7 @@ UG_F32, UG_BF16 = 0, 1
 UG_PLAN_HOST_ONLY = 1
 
 EXPORTED = ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_permute", "ug_unpermute",
-            "ug_rope2d", "ug_attn_fwd", "ug_status_str", "ug_last_error")
+            "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_status_str", "ug_last_error")
 
 
 class UgDesc(ctypes.Structure):
@@ -63,12 +63,14 @@ def lib():
         L.ug_unpermute.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
         L.ug_rope2d.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
         L.ug_attn_fwd.argtypes = [c_void_p] * 7
+        L.ug_attn_fwd_raster.argtypes = [c_void_p] * 7
+        L.ug_permute_rope.argtypes = [c_void_p] * 6
         L.ug_status_str.argtypes = [c_int32]
         L.ug_status_str.restype = c_char_p
         L.ug_last_error.argtypes = []
         L.ug_last_error.restype = c_char_p
         for name in ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_permute", "ug_unpermute",
-                     "ug_rope2d", "ug_attn_fwd"):
+                     "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster"):
             getattr(L, name).restype = c_int32
         _lib = L
     return _lib
@@ -223,19 +225,59 @@ def ug_attn_fwd(plan: Plan, q, k, v, o=None, workspace=None):
     return o
 
 
-class Layer:
-    """One attention layer's whole path with preallocated buffers:
-    permute Q, K, V -> RoPE on Q, K -> attention -> unpermute O."""
+def ug_permute_rope(plan: Plan, q_raster, k_raster, q_perm=None, k_perm=None):
+    _check_tensor(plan, q_raster, "q_raster")
+    _check_tensor(plan, k_raster, "k_raster")
+    if q_perm is None:
+        q_perm = _torch().empty_like(q_raster)
+    if k_perm is None:
+        k_perm = _torch().empty_like(k_raster)
+    _check_tensor(plan, q_perm, "q_perm")
+    _check_tensor(plan, k_perm, "k_perm")
+    _check("ug_permute_rope", lib().ug_permute_rope(plan.handle, c_void_p(q_raster.data_ptr()),
+                                                    c_void_p(k_raster.data_ptr()), c_void_p(q_perm.data_ptr()),
+                                                    c_void_p(k_perm.data_ptr()), _stream_ptr(q_raster)))
+    return q_perm, k_perm
 
-    def __init__(self, plan: Plan, device="cuda"):
+
+def ug_attn_fwd_raster(plan: Plan, q, k, v, o_raster=None, workspace=None):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(plan, t, n)
+    if o_raster is None:
+        o_raster = _torch().empty_like(q)
+    _check_tensor(plan, o_raster, "o_raster")
+    ws = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p()
+    _check("ug_attn_fwd_raster", lib().ug_attn_fwd_raster(plan.handle, c_void_p(q.data_ptr()), c_void_p(k.data_ptr()),
+                                                          c_void_p(v.data_ptr()), c_void_p(o_raster.data_ptr()), ws,
+                                                          _stream_ptr(q)))
+    return o_raster
+
+
+class Layer:
+    """One attention layer's whole path with preallocated buffers.
+
+    fused=False: permute Q, K, V -> RoPE on Q, K -> attention -> unpermute O
+    (one call per step of the path).  fused=True: permute+RoPE of Q and K in
+    one pass, permute V, attention writing O straight in raster order; the
+    result is bit-identical.
+    """
+
+    def __init__(self, plan: Plan, device="cuda", fused=False):
         torch = _torch()
         self.plan = plan
+        self.fused = fused
         dt = torch.bfloat16 if plan.desc.dtype == UG_BF16 else torch.float32
         mk = lambda: torch.empty(plan.shape, dtype=dt, device=device)
-        self.qp, self.kp, self.vp, self.op = mk(), mk(), mk(), mk()
+        self.qp, self.kp, self.vp = mk(), mk(), mk()
+        self.op = None if fused else mk()
 
     def __call__(self, q, k, v, out):
         p = self.plan
+        if self.fused:
+            ug_permute_rope(p, q, k, self.qp, self.kp)
+            ug_permute(p, v, self.vp)
+            ug_attn_fwd_raster(p, self.qp, self.kp, self.vp, out)
+            return out
         ug_permute(p, q, self.qp)
         ug_permute(p, k, self.kp)
         ug_permute(p, v, self.vp)

@@ -158,6 +158,102 @@ __global__ __launch_bounds__(1024) void rope2d_kernel(T* __restrict__ q, T* __re
 }
 
 // ---------------------------------------------------------------------------
+// Fused window-first permutation + 2D axial RoPE of Q and K: permuted row j
+// reads raster row map(j) of both tensors, rotates HR and LR rows exactly as
+// rope2d_kernel does (same table, same fp32 arithmetic, so the result is
+// bit-identical to permute followed by rope2d) and copies text rows as they
+// are.  One read and one write of Q and K instead of two of each.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(1024) void permute_rope_kernel(const T* __restrict__ qsrc, const T* __restrict__ ksrc,
+                                                            T* __restrict__ qdst, T* __restrict__ kdst, int32_t L,
+                                                            int32_t T0, int32_t N, int32_t W, int32_t lr_w,
+                                                            int32_t rho, int32_t heads, int32_t D,
+                                                            const int32_t* __restrict__ perm,
+                                                            const float2* __restrict__ cs) {
+  constexpr int E = 16 / sizeof(T);
+  const int32_t units_per_head = D / E;
+  const int32_t units = heads * units_per_head;
+  const int32_t j0 = blockIdx.x * kRopeRows;
+  const int64_t boff = int64_t(blockIdx.y) * L * units;
+  const u32x4* const qs = reinterpret_cast<const u32x4*>(qsrc) + boff;
+  const u32x4* const ks = reinterpret_cast<const u32x4*>(ksrc) + boff;
+  u32x4* const qd = reinterpret_cast<u32x4*>(qdst) + boff;
+  u32x4* const kd = reinterpret_cast<u32x4*>(kdst) + boff;
+  int32_t src[kRopeRows], pr[kRopeRows], pc[kRopeRows];
+#pragma unroll
+  for (int r = 0; r < kRopeRows; ++r) {
+    const int32_t j = min(j0 + r, L - 1);
+    src[r] = j;
+    pr[r] = -1;  // text: not rotated
+    pc[r] = 0;
+    if (j >= T0 && j < T0 + N) {
+      const int32_t idx = perm[j - T0];
+      src[r] = T0 + idx;
+      pr[r] = idx / W;
+      pc[r] = idx - pr[r] * W;
+    } else if (j >= T0 + N) {
+      const int32_t i = j - T0 - N;
+      const int32_t m = i / lr_w;
+      pr[r] = rho * m;
+      pc[r] = rho * (i - m * lr_w);
+    }
+  }
+  for (int32_t c = threadIdx.x; c < units; c += blockDim.x) {
+    const int32_t e0 = (c % units_per_head) * E;
+    const bool col = e0 >= D / 2;
+    const int32_t k0 = (col ? e0 - D / 2 : e0) / 2;
+    u32x4 qa[kRopeRows], ka[kRopeRows];
+#pragma unroll
+    for (int r = 0; r < kRopeRows; ++r) {
+      if (j0 + r < L) {
+        qa[r] = __builtin_nontemporal_load(qs + int64_t(src[r]) * units + c);
+        ka[r] = __builtin_nontemporal_load(ks + int64_t(src[r]) * units + c);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRopeRows; ++r) {
+      if (j0 + r >= L) continue;
+      if (pr[r] >= 0) {
+        const float2* tab = cs + int64_t(col ? pc[r] : pr[r]) * (D / 4) + k0;
+        if constexpr (std::is_same<T, float>::value) {
+          float* x = reinterpret_cast<float*>(&qa[r]);
+          float* y = reinterpret_cast<float*>(&ka[r]);
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const float2 t = tab[p];
+            const float a = x[2 * p], b = x[2 * p + 1];
+            x[2 * p] = a * t.x - b * t.y;
+            x[2 * p + 1] = a * t.y + b * t.x;
+            const float a2 = y[2 * p], b2 = y[2 * p + 1];
+            y[2 * p] = a2 * t.x - b2 * t.y;
+            y[2 * p + 1] = a2 * t.y + b2 * t.x;
+          }
+        } else {
+          bf16x8 x = *reinterpret_cast<bf16x8*>(&qa[r]);
+          bf16x8 y = *reinterpret_cast<bf16x8*>(&ka[r]);
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const float2 t = tab[p];
+            const float a = float(x[2 * p]), b = float(x[2 * p + 1]);
+            x[2 * p] = __bf16(a * t.x - b * t.y);
+            x[2 * p + 1] = __bf16(a * t.y + b * t.x);
+            const float a2 = float(y[2 * p]), b2 = float(y[2 * p + 1]);
+            y[2 * p] = __bf16(a2 * t.x - b2 * t.y);
+            y[2 * p + 1] = __bf16(a2 * t.y + b2 * t.x);
+          }
+          qa[r] = *reinterpret_cast<u32x4*>(&x);
+          ka[r] = *reinterpret_cast<u32x4*>(&y);
+        }
+      }
+      const int64_t off = int64_t(j0 + r) * units + c;
+      __builtin_nontemporal_store(qa[r], qd + off);
+      __builtin_nontemporal_store(ka[r], kd + off);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Composite-masked attention forward (关键设计 3 with the mask of 关键设计 2).
 //
 // One workgroup = one query tile (<= 256 permuted rows sharing one key set)
@@ -211,6 +307,8 @@ struct AttnParams {
   const ug::Range* ranges;
   const ug::Block* blocks;
   float scale_log2;      // log2(e) / sqrt(D)
+  int32_t T, N;          // text rows, HR rows
+  const int32_t* out_perm;  // non-null: write HR output row T+i to raster row T+out_perm[i]
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -607,7 +705,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
     const int cc = lane % Lds::kChunks;
     const uint4 val = *reinterpret_cast<const uint4*>(ost + r * RB + ((cc ^ Lds::k_swz(r)) * 16));
     const int32_t row = task.q0 + wave * 32 + r;
-    if (row < task.q1) *reinterpret_cast<uint4*>(og + row * rs + cc * Lds::kEl16) = val;
+    if (row < task.q1) {
+      const int32_t orow = (p.out_perm && row >= p.T && row < p.T + p.N) ? p.T + p.out_perm[row - p.T] : row;
+      *reinterpret_cast<uint4*>(og + orow * rs + cc * Lds::kEl16) = val;
+    }
   }
 }
 
@@ -670,6 +771,49 @@ void launch_attn(ug_plan_t p, const AttnParams& ap, hipStream_t s) {
   hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3(unsigned(p->blocks.size())), dim3(kAttnThreads), 0, s, ap);
 }
 
+ug_status attn_common(ug_plan_t p, const void* q, const void* k, const void* v, void* o, void* workspace,
+                      void* stream, bool raster_out, const char* fn) {
+  ug::clear_error();
+  (void)workspace;
+  ug_status st = check_plan(p, fn);
+  if (st != UG_OK) return st;
+  if (!q || !k || !v || !o) return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": NULL tensor");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": tensors must be 16-byte aligned");
+  const int64_t n = tensor_bytes(p);
+  if (overlap(o, q, n) || overlap(o, k, n) || overlap(o, v, n))
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": o overlaps q, k or v");
+  if (current_device() != p->device)
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": current device is not the plan's device");
+  if (p->blocks.empty()) return UG_OK;
+  AttnParams ap{};
+  ap.q = q;
+  ap.k = k;
+  ap.v = v;
+  ap.o = o;
+  ap.row_stride = int64_t(p->d.heads) * p->d.head_dim;
+  ap.batch_stride = p->L * ap.row_stride;
+  ap.heads = p->d.heads;
+  ap.tasks = p->d_tasks;
+  ap.ranges = p->d_ranges;
+  ap.blocks = p->d_blocks;
+  ap.scale_log2 = float(1.4426950408889634 / std::sqrt(double(p->d.head_dim)));
+  ap.T = int32_t(p->T);
+  ap.N = int32_t(p->N);
+  ap.out_perm = raster_out ? p->d_perm : nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = p->d.dtype == UG_BF16;
+  if (bf && p->d.head_dim == 128)
+    launch_attn<__bf16, 128>(p, ap, s);
+  else if (bf && p->d.head_dim == 64)
+    launch_attn<__bf16, 64>(p, ap, s);
+  else if (!bf && p->d.head_dim == 128)
+    launch_attn<float, 128>(p, ap, s);
+  else
+    launch_attn<float, 64>(p, ap, s);
+  return launch_status(fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -715,42 +859,50 @@ ug_status ug_rope2d(ug_plan_t p, void* q_perm, void* k_perm, void* stream) {
 
 ug_status ug_attn_fwd(ug_plan_t p, const void* q, const void* k, const void* v, void* o, void* workspace,
                       void* stream) {
+  return attn_common(p, q, k, v, o, workspace, stream, false, "ug_attn_fwd");
+}
+
+ug_status ug_attn_fwd_raster(ug_plan_t p, const void* q, const void* k, const void* v, void* o_raster,
+                             void* workspace, void* stream) {
+  return attn_common(p, q, k, v, o_raster, workspace, stream, true, "ug_attn_fwd_raster");
+}
+
+ug_status ug_permute_rope(ug_plan_t p, const void* q_raster, const void* k_raster, void* q_perm, void* k_perm,
+                          void* stream) {
   ug::clear_error();
-  (void)workspace;
-  ug_status st = check_plan(p, "ug_attn_fwd");
+  ug_status st = check_plan(p, "ug_permute_rope");
   if (st != UG_OK) return st;
-  if (!q || !k || !v || !o) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_fwd: NULL tensor");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_fwd: tensors must be 16-byte aligned");
+  if (!q_raster || !k_raster || !q_perm || !k_perm)
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_permute_rope: NULL tensor");
+  if (!aligned16(q_raster) || !aligned16(k_raster) || !aligned16(q_perm) || !aligned16(k_perm))
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_permute_rope: tensors must be 16-byte aligned");
   const int64_t n = tensor_bytes(p);
-  if (overlap(o, q, n) || overlap(o, k, n) || overlap(o, v, n))
-    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_fwd: o overlaps q, k or v");
+  const void* ins[2] = {q_raster, k_raster};
+  const void* outs[2] = {q_perm, k_perm};
+  for (const void* a : outs)
+    for (const void* b : ins)
+      if (overlap(a, b, n)) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_permute_rope: an output overlaps an input");
+  if (overlap(q_perm, k_perm, n)) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_permute_rope: q_perm and k_perm overlap");
   if (current_device() != p->device)
-    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_fwd: current device is not the plan's device");
-  if (p->blocks.empty()) return UG_OK;
-  AttnParams ap{};
-  ap.q = q;
-  ap.k = k;
-  ap.v = v;
-  ap.o = o;
-  ap.row_stride = int64_t(p->d.heads) * p->d.head_dim;
-  ap.batch_stride = p->L * ap.row_stride;
-  ap.heads = p->d.heads;
-  ap.tasks = p->d_tasks;
-  ap.ranges = p->d_ranges;
-  ap.blocks = p->d_blocks;
-  ap.scale_log2 = float(1.4426950408889634 / std::sqrt(double(p->d.head_dim)));
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_permute_rope: current device is not the plan's device");
+  const int E = p->d.dtype == UG_BF16 ? 8 : 4;
+  const int64_t units = int64_t(p->d.heads) * p->d.head_dim / E;
+  const dim3 grid(unsigned((p->L + kRopeRows - 1) / kRopeRows), unsigned(p->d.batch));
+  const unsigned threads = unsigned(std::min<int64_t>(1024, (units + 63) / 64 * 64));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool bf = p->d.dtype == UG_BF16;
-  if (bf && p->d.head_dim == 128)
-    launch_attn<__bf16, 128>(p, ap, s);
-  else if (bf && p->d.head_dim == 64)
-    launch_attn<__bf16, 64>(p, ap, s);
-  else if (!bf && p->d.head_dim == 128)
-    launch_attn<float, 128>(p, ap, s);
+  const float2* cs = reinterpret_cast<const float2*>(p->d_rope);
+  const int32_t lr_w = std::max(p->d.lr_w, 1);
+  if (p->d.dtype == UG_BF16)
+    hipLaunchKernelGGL(permute_rope_kernel<__bf16>, grid, dim3(threads), 0, s, static_cast<const __bf16*>(q_raster),
+                       static_cast<const __bf16*>(k_raster), static_cast<__bf16*>(q_perm),
+                       static_cast<__bf16*>(k_perm), int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w,
+                       p->d.rho, p->d.heads, p->d.head_dim, p->d_perm, cs);
   else
-    launch_attn<float, 64>(p, ap, s);
-  return launch_status("ug_attn_fwd");
+    hipLaunchKernelGGL(permute_rope_kernel<float>, grid, dim3(threads), 0, s, static_cast<const float*>(q_raster),
+                       static_cast<const float*>(k_raster), static_cast<float*>(q_perm), static_cast<float*>(k_perm),
+                       int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w, p->d.rho, p->d.heads,
+                       p->d.head_dim, p->d_perm, cs);
+  return launch_status("ug_permute_rope");
 }
 
 }  // extern "C"

@@ -61,8 +61,8 @@ typedef enum ug_dtype { UG_F32 = 0, UG_BF16 = 1 } ug_dtype;
  *  - lr_h x lr_w: LR guidance grid (关键设计 2: X_lr in R^{h x w}); given
  *    explicitly (0 x anything = no LR tokens).  LR token (m, n) takes RoPE
  *    position (rho*m, rho*n) (关键设计 2, the coordinate-scaling equation).
- *  - window: l, the window side in tokens (l = 16 in 关键设计 1).  The GPU
- *    kernels need l*l <= 256.
+ *  - window: l, the window side in tokens (l = 16 in 关键设计 1).  Windows
+ *    of more than 256 tokens are split into several query tiles.
  *  - radius: HR queries see HR keys whose window is within Chebyshev
  *    distance `radius` of their own (1 = own + adjacent windows, 3x3).
  *  - rope_theta: base of the axial RoPE frequencies omega_k =
@@ -162,6 +162,24 @@ ug_status ug_rope2d(ug_plan_t plan, void* q_perm, void* k_perm, void* stream);
  */
 ug_status ug_attn_fwd(ug_plan_t plan, const void* q, const void* k, const void* v, void* o,
                       void* workspace, void* stream);
+
+/*
+ * Fused forms of the same path (one fewer HBM pass each; results are
+ * bit-identical to the separate calls):
+ *
+ * ug_permute_rope: q_perm/k_perm = ug_permute of q_raster/k_raster followed
+ * by ug_rope2d, in one read and one write of Q and K (window-first order of
+ * 关键设计 1 and the scaled-position RoPE of 关键设计 2).  Out of place: no
+ * output may overlap an input, and q_perm must not overlap k_perm.
+ *
+ * ug_attn_fwd_raster: ug_attn_fwd with the output written in the raster
+ * layout, i.e. ug_attn_fwd followed by ug_unpermute, without the extra pass.
+ * Same arguments and rules as ug_attn_fwd; o_raster must not overlap q, k, v.
+ */
+ug_status ug_permute_rope(ug_plan_t plan, const void* q_raster, const void* k_raster, void* q_perm,
+                          void* k_perm, void* stream);
+ug_status ug_attn_fwd_raster(ug_plan_t plan, const void* q, const void* k, const void* v, void* o_raster,
+                             void* workspace, void* stream);
 
 const char* ug_status_str(ug_status s);
 const char* ug_last_error(void);

@@ -109,14 +109,15 @@ def test_attention_matches_oracle(U, name, qscale):
         assert_close(seg_errors(got[:, h], oracle_attn_only(w, h), w), tol_of(w), f"{name} x{qscale} head {h}")
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("name", SMALL)
-def test_full_layer_matches_oracle(U, name):
+def test_full_layer_matches_oracle(U, name, fused):
     import torch
     w = WL.WORKLOADS[name]
     p = plan_of(U, w)
     q, k, v = qkv_device(w)
     out = torch.empty_like(q)
-    U.Layer(p)(q, k, v, out)
+    U.Layer(p, fused=fused)(q, k, v, out)
     torch.cuda.synchronize()
     got = to_host_f64(out, w.dtype)[0]
     geo = O.geometry_of(w)
@@ -138,16 +139,18 @@ def sample_rows(w, seed=0):
     return np.unique(np.asarray(rows, np.int64))
 
 
-@pytest.mark.parametrize("name", ["2k", "ragged", "4k", "8k"])
-def test_full_size_sampled_rows(U, name):
-    """The bench's launch configuration at full size; the oracle recomputes
-    sampled rows one by one (text, corner/edge/interior HR windows, LR)."""
+@pytest.mark.parametrize("name,fused", [("2k", True), ("ragged", True), ("4k", True), ("4k", False),
+                                        ("8k", True)])
+def test_full_size_sampled_rows(U, name, fused):
+    """The bench's launch configuration (fused layer) at full size; the
+    oracle recomputes sampled rows one by one (text, corner/edge/interior HR
+    windows, LR)."""
     import torch
     w = WL.WORKLOADS[name]
     p = plan_of(U, w)
     q, k, v = qkv_device(w)
     out = torch.empty_like(q)
-    U.Layer(p)(q, k, v, out)
+    U.Layer(p, fused=fused)(q, k, v, out)
     torch.cuda.synchronize()
     geo = O.geometry_of(w)
     rows = sample_rows(w)
@@ -156,6 +159,26 @@ def test_full_size_sampled_rows(U, name):
         ref = O.forward_rows(geo, *(WL.head_f64(w, t, h) for t in (WL.Q, WL.K, WL.V)), w.rope_theta, rows)
         assert_close(seg_errors(got, ref, w, rows), tol_of(w), f"{name} head {h}")
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_ragged", "small_d64", "small_ragged_f32", "1k", "ragged"])
+def test_fused_entry_points_bit_exact(U, name):
+    """ug_permute_rope == ug_permute + ug_rope2d and ug_attn_fwd_raster ==
+    ug_attn_fwd + ug_unpermute, bit for bit."""
+    import torch
+    w = WL.WORKLOADS[name]
+    p = plan_of(U, w)
+    q, k, v = qkv_device(w)
+    qp, kp = U.ug_permute(p, q), U.ug_permute(p, k)
+    U.ug_rope2d(p, qp, kp)
+    qf, kf = U.ug_permute_rope(p, q, k)
+    vp = U.ug_permute(p, v)
+    o_sep = U.ug_unpermute(p, U.ug_attn_fwd(p, qp, kp, vp))
+    o_fused = U.ug_attn_fwd_raster(p, qp, kp, vp)
+    torch.cuda.synchronize()
+    as_bits = (lambda t: t.view(torch.int16)) if w.dtype == "bf16" else (lambda t: t.view(torch.int32))
+    assert torch.equal(as_bits(qf), as_bits(qp)) and torch.equal(as_bits(kf), as_bits(kp))
+    assert torch.equal(as_bits(o_fused), as_bits(o_sep))
 
 
 def test_attention_is_deterministic(U):
@@ -193,7 +216,7 @@ def test_edge_cases(U, case, dtype):
     p = plan_of(U, w)
     q, k, v = qkv_device(w)
     out = torch.empty_like(q)
-    U.Layer(p)(q, k, v, out)
+    U.Layer(p, fused=(case in ("batch2", "no_lr")))(q, k, v, out)
     torch.cuda.synchronize()
     geo = O.geometry_of(w)
     for b in range(w.batch):
@@ -217,5 +240,9 @@ def test_argument_errors_on_device(U):
     assert lib.ug_attn_fwd(p.handle, vp(q.data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()), vp(q.data_ptr()),
                            None, s) == 1
     assert lib.ug_rope2d(p.handle, vp(q.data_ptr()), vp(q.data_ptr()), s) == 1
+    assert lib.ug_permute_rope(p.handle, vp(q.data_ptr()), vp(k.data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()),
+                               s) == 1
+    assert lib.ug_attn_fwd_raster(p.handle, vp(q.data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()), vp(v.data_ptr()),
+                                  None, s) == 1
     with pytest.raises(ValueError):
         U.ug_permute(p, q[:, :10].contiguous())
