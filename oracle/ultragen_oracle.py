@@ -37,6 +37,11 @@ open (all listed in the design doc's table of readings):
   R7 "adjacent" = Chebyshev window distance <= radius (radius 1 = 3x3 windows);
   R8 HR queries see ALL LR tokens; LR queries see LR and text; text queries see
      text and HR, not LR.
+  R8' (variant, lr_mode = 1) [KD2] says HR tokens attend to the
+     *corresponding* LR anchors: an LR token corresponds to the window that
+     contains its scaled position (rho*m, rho*n); an HR query sees the LR
+     tokens of the windows within its neighbourhood radius, exactly like its
+     HR keys.
 """
 from __future__ import annotations
 
@@ -59,6 +64,7 @@ class Geometry:
     window: int
     radius: int
     rho: int
+    lr_mode: int = 0   # 0: HR sees all LR (R8); 1: corresponding LR only (R8')
 
     @property
     def n_hr(self):
@@ -78,27 +84,28 @@ class Geometry:
         return (-(-self.hr_h // self.window), -(-self.hr_w // self.window))
 
 
-def geometry(hr_h, hr_w, n_text, window=16, radius=1, rho=4, lr_h=None, lr_w=None) -> Geometry:
+def geometry(hr_h, hr_w, n_text, window=16, radius=1, rho=4, lr_h=None, lr_w=None, lr_mode=0) -> Geometry:
     """LR grid defaults to ceil(H/rho) x ceil(W/rho), since rho = H/h ([KD2], R3);
     an explicit 0 means no LR tokens."""
     if lr_h is None:
         lr_h = -(-hr_h // rho)
     if lr_w is None:
         lr_w = -(-hr_w // rho)
-    return Geometry(hr_h, hr_w, lr_h, lr_w, n_text, window, radius, rho)
+    return Geometry(hr_h, hr_w, lr_h, lr_w, n_text, window, radius, rho, lr_mode)
 
 
 def geometry_of(w) -> Geometry:
     """Geometry of a workloads.Workload (duck-typed)."""
-    return geometry(w.hr_h, w.hr_w, w.n_text, w.window, w.radius, w.rho, w.lr_h, w.lr_w)
+    return geometry(w.hr_h, w.hr_w, w.n_text, w.window, w.radius, w.rho, w.lr_h, w.lr_w,
+                    getattr(w, "lr_mode", 0))
 
 
 def token_coords(g: Geometry):
     """Per raster row: kind, RoPE position (row, col) and HR window (wy, wx).
 
     HR token r*W + c sits at (r, c) in window (r // l, c // l) [KD1]; LR token
-    m*w + n sits at (rho*m, rho*n) [KD2]; text sits at (0, 0) (R4).  Window
-    coordinates of non-HR rows are -1.
+    m*w + n sits at (rho*m, rho*n) [KD2], in the window containing that
+    position (R8'); text sits at (0, 0) (R4) and has window -1.
     """
     L = g.seq_len
     kind = np.empty(L, np.int64)
@@ -113,8 +120,10 @@ def token_coords(g: Geometry):
     r, c = np.divmod(np.arange(N), g.hr_w)
     pr[T:T + N], pc[T:T + N] = r, c
     wy[T:T + N], wx[T:T + N] = r // g.window, c // g.window
-    m, n = np.divmod(np.arange(g.n_lr), g.lr_w)
-    pr[T + N:], pc[T + N:] = g.rho * m, g.rho * n
+    if g.n_lr:
+        m, n = np.divmod(np.arange(g.n_lr), g.lr_w)
+        pr[T + N:], pc[T + N:] = g.rho * m, g.rho * n
+        wy[T + N:], wx[T + N:] = g.rho * m // g.window, g.rho * n // g.window
     return kind, pr, pc, wy, wx
 
 
@@ -144,6 +153,29 @@ def window_offsets(hr_h: int, hr_w: int, window: int) -> np.ndarray:
             hx = min(window, hr_w - b * window)
             sizes.append(hy * hx)
     return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+
+
+def lr_window_first_perm(g: Geometry) -> np.ndarray:
+    """LR tokens grouped by the window containing their scaled position
+    (R8'), windows row-major, tokens row-major inside; LR tokens whose
+    position falls outside the HR window grid come last, in raster order."""
+    gy, gx = g.grid
+    m, n = np.divmod(np.arange(g.n_lr), g.lr_w)
+    a, b = g.rho * m // g.window, g.rho * n // g.window
+    outside = ((a >= gy) | (b >= gx)).astype(np.int64)
+    win = np.where(outside == 1, 0, a * gx + b)
+    return np.lexsort((n, m, win, outside)).astype(np.int64)
+
+
+def lr_window_offsets(g: Geometry) -> np.ndarray:
+    """Start of each window's LR tokens in the LR window-first order; the
+    last entry is where the out-of-grid tail starts (then n_lr follows)."""
+    gy, gx = g.grid
+    m, n = np.divmod(np.arange(g.n_lr), g.lr_w)
+    a, b = g.rho * m // g.window, g.rho * n // g.window
+    inside = (a < gy) & (b < gx)
+    counts = np.bincount((a * gx + b)[inside], minlength=gy * gx)
+    return np.concatenate([[0], np.cumsum(counts), [g.n_lr]]).astype(np.int64)
 
 
 def neighbour_windows(hr_h: int, hr_w: int, window: int, radius: int):
@@ -201,8 +233,9 @@ def allowed_keys_of(g: Geometry, coords, i: int) -> np.ndarray:
     elif kind[i] == LR:
         ok = (kind == LR) | (kind == TEXT)
     else:
-        near = (np.maximum(np.abs(wy - wy[i]), np.abs(wx - wx[i])) <= g.radius) & (kind == HR)
-        ok = (kind == TEXT) | (kind == LR) | near
+        near = np.maximum(np.abs(wy - wy[i]), np.abs(wx - wx[i])) <= g.radius
+        lr_ok = (kind == LR) & (near if g.lr_mode == 1 else True)
+        ok = (kind == TEXT) | lr_ok | (near & (kind == HR))
     return np.nonzero(ok)[0]
 
 
@@ -210,12 +243,15 @@ def allowed_dense(g: Geometry) -> np.ndarray:
     """Explicit L x L boolean mask (small grids only)."""
     kind, _, _, wy, wx = token_coords(g)
     qt, kt = kind[:, None], kind[None, :]
-    hr_near = (np.maximum(np.abs(wy[:, None] - wy[None, :]), np.abs(wx[:, None] - wx[None, :]))
-               <= g.radius) & (qt == HR) & (kt == HR)
+    near = np.maximum(np.abs(wy[:, None] - wy[None, :]), np.abs(wx[:, None] - wx[None, :])) <= g.radius
+    hr_near = near & (qt == HR) & (kt == HR)
     text_q = (qt == TEXT) & ((kt == TEXT) | (kt == HR))
     lr_q = (qt == LR) & ((kt == LR) | (kt == TEXT))
-    hr_q = (qt == HR) & ((kt == TEXT) | (kt == LR))
-    return text_q | lr_q | hr_q | hr_near
+    hr_lr = (qt == HR) & (kt == LR)
+    if g.lr_mode == 1:
+        hr_lr = hr_lr & near
+    hr_q = (qt == HR) & (kt == TEXT)
+    return text_q | lr_q | hr_q | hr_lr | hr_near
 
 
 def pair_count(g: Geometry) -> int:
@@ -225,14 +261,18 @@ def pair_count(g: Geometry) -> int:
     total = T * (T + N) + Nl * (Nl + T)
     off = window_offsets(g.hr_h, g.hr_w, g.window)
     size = np.diff(off)
+    lr_size = np.diff(lr_window_offsets(g))[:-1] if Nl else np.zeros(size.size, np.int64)
     gy, gx = g.grid
     for a in range(gy):
         for b in range(gx):
             seen = 0
+            lr_seen = 0
             for a2 in range(max(0, a - g.radius), min(gy, a + g.radius + 1)):
                 for b2 in range(max(0, b - g.radius), min(gx, b + g.radius + 1)):
                     seen += int(size[a2 * gx + b2])
-            total += int(size[a * gx + b]) * (T + Nl + seen)
+                    lr_seen += int(lr_size[a2 * gx + b2])
+            lr_keys = lr_seen if g.lr_mode == 1 else Nl
+            total += int(size[a * gx + b]) * (T + lr_keys + seen)
     return total
 
 

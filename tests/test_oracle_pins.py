@@ -274,3 +274,54 @@ def test_mask_structure_on_tiny_masked():
     corner = T + 0
     assert counts[centre] == T + Nl + 9 * 256
     assert counts[corner] == T + Nl + 4 * 256
+
+
+# ---------------------------------------------------------------- corresponding-LR variant
+
+def test_corresponding_lr_hand_worked():
+    g = golden("corresponding_lr_8x8_l4_rho2.json")
+    geo = O.geometry(g["hr_h"], g["hr_w"], g["n_text"], g["window"], g["radius"], g["rho"], g["lr_h"], g["lr_w"],
+                     g["lr_mode"])
+    assert O.lr_window_first_perm(geo).tolist() == g["lr_perm"]
+    assert O.lr_window_offsets(geo).tolist() == g["lr_win_off"]
+    dense = O.allowed_dense(geo)
+    coords = O.token_coords(geo)
+    for row, keys in g["allowed"].items():
+        assert np.nonzero(dense[int(row)])[0].tolist() == keys
+        assert O.allowed_keys_of(geo, coords, int(row)).tolist() == keys
+    assert O.pair_count(geo) == int(dense.sum())
+
+
+def test_corresponding_lr_closed_form_4k():
+    pins = golden("pair_counts.json")["corresponding_lr_4k"]
+    w = WORKLOADS["4k"]
+    g1 = O.geometry(w.hr_h, w.hr_w, w.n_text, w.window, w.radius, w.rho, w.lr_h, w.lr_w, 1)
+    g0 = O.geometry(w.hr_h, w.hr_w, w.n_text, w.window, w.radius, w.rho, w.lr_h, w.lr_w, 0)
+    assert O.pair_count(g1) == pins["total"]
+    assert O.pair_count(g0) - O.pair_count(g1) == w.n_hr * w.n_lr - pins["hr_to_lr"]
+    off = O.lr_window_offsets(g1)
+    assert np.all(np.diff(off)[:-1] == 16) and off[-1] == off[-2] == w.n_lr
+
+
+@pytest.mark.parametrize("H,W,lh,lw,l,rho,r", [(48, 40, 12, 10, 16, 4, 1), (37, 45, 10, 12, 16, 4, 1),
+                                              (30, 30, 11, 11, 8, 3, 0), (20, 28, 8, 9, 8, 4, 2)])
+def test_corresponding_lr_dense_vs_grouped_and_library(H, W, lh, lw, l, rho, r):
+    """Both oracle modes agree and match torch SDPA given the variant's mask;
+    the LR window-first order is a bijection grouping LR tokens by window."""
+    geo = O.geometry(H, W, 7, l, r, rho, lh, lw, 1)
+    rng = np.random.default_rng(31)
+    L, D = geo.seq_len, 32
+    q, k, v = (rng.standard_normal((L, D)) for _ in range(3))
+    dense = O.forward_head(geo, q, k, v, 1e4, "dense")
+    grouped = O.forward_head(geo, q, k, v, 1e4, "grouped")
+    qr, kr = O.rotate_head(geo, q, 1e4), O.rotate_head(geo, k, 1e4)
+    assert np.allclose(dense, grouped, atol=1e-12)
+    assert np.allclose(dense, _sdpa(qr, kr, v, O.allowed_dense(geo)), atol=1e-12)
+    perm = O.lr_window_first_perm(geo)
+    assert np.array_equal(np.sort(perm), np.arange(geo.n_lr))
+    off = O.lr_window_offsets(geo)
+    _, _, _, wy, wx = O.token_coords(geo)
+    gy, gx = geo.grid
+    lw_ = (wy * gx + wx)[geo.n_text + geo.n_hr:][perm]
+    for wdx in range(gy * gx):
+        assert np.all(lw_[off[wdx]:off[wdx + 1]] == wdx)
