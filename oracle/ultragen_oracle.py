@@ -41,7 +41,10 @@ open (all listed in the design doc's table of readings):
      *corresponding* LR anchors: an LR token corresponds to the window that
      contains its scaled position (rho*m, rho*n); an HR query sees the LR
      tokens of the windows within its neighbourhood radius, exactly like its
-     HR keys.
+     HR keys.  An LR token whose scaled position lies beyond the window grid
+     (only possible when the LR grid is given larger than ceil(H/rho) x
+     ceil(W/rho)) is inside no window, so it corresponds to none and no HR
+     query sees it; LR queries still see it.
 """
 from __future__ import annotations
 
@@ -225,6 +228,13 @@ def rope_rotate(x: np.ndarray, pos_r: np.ndarray, pos_c: np.ndarray, theta: floa
 # The composite mask ([KD2], [GS-B], [KD3]; R6-R8)
 # --------------------------------------------------------------------------
 
+def _in_window_grid(g: Geometry, wy, wx) -> np.ndarray:
+    """Whether a token's window (wy, wx) is one of the gy x gx grid windows
+    (R8': an LR anchor beyond the grid belongs to no window)."""
+    gy, gx = g.grid
+    return (wy >= 0) & (wy < gy) & (wx >= 0) & (wx < gx)
+
+
 def allowed_keys_of(g: Geometry, coords, i: int) -> np.ndarray:
     """Raster indices of the keys query row i may attend to."""
     kind, _, _, wy, wx = coords
@@ -234,7 +244,7 @@ def allowed_keys_of(g: Geometry, coords, i: int) -> np.ndarray:
         ok = (kind == LR) | (kind == TEXT)
     else:
         near = np.maximum(np.abs(wy - wy[i]), np.abs(wx - wx[i])) <= g.radius
-        lr_ok = (kind == LR) & (near if g.lr_mode == 1 else True)
+        lr_ok = (kind == LR) & (near & _in_window_grid(g, wy, wx) if g.lr_mode == 1 else True)
         ok = (kind == TEXT) | lr_ok | (near & (kind == HR))
     return np.nonzero(ok)[0]
 
@@ -249,7 +259,7 @@ def allowed_dense(g: Geometry) -> np.ndarray:
     lr_q = (qt == LR) & ((kt == LR) | (kt == TEXT))
     hr_lr = (qt == HR) & (kt == LR)
     if g.lr_mode == 1:
-        hr_lr = hr_lr & near
+        hr_lr = hr_lr & near & _in_window_grid(g, wy, wx)[None, :]
     hr_q = (qt == HR) & (kt == TEXT)
     return text_q | lr_q | hr_q | hr_lr | hr_near
 

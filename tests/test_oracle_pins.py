@@ -278,8 +278,9 @@ def test_mask_structure_on_tiny_masked():
 
 # ---------------------------------------------------------------- corresponding-LR variant
 
-def test_corresponding_lr_hand_worked():
-    g = golden("corresponding_lr_8x8_l4_rho2.json")
+@pytest.mark.parametrize("fixture", ["corresponding_lr_8x8_l4_rho2.json", "corresponding_lr_overhang_4x4_l2_rho2.json"])
+def test_corresponding_lr_hand_worked(fixture):
+    g = golden(fixture)
     geo = O.geometry(g["hr_h"], g["hr_w"], g["n_text"], g["window"], g["radius"], g["rho"], g["lr_h"], g["lr_w"],
                      g["lr_mode"])
     assert O.lr_window_first_perm(geo).tolist() == g["lr_perm"]
@@ -290,6 +291,8 @@ def test_corresponding_lr_hand_worked():
         assert np.nonzero(dense[int(row)])[0].tolist() == keys
         assert O.allowed_keys_of(geo, coords, int(row)).tolist() == keys
     assert O.pair_count(geo) == int(dense.sum())
+    if "pairs" in g:
+        assert O.pair_count(geo) == g["pairs"]
 
 
 def test_corresponding_lr_closed_form_4k():
@@ -304,7 +307,8 @@ def test_corresponding_lr_closed_form_4k():
 
 
 @pytest.mark.parametrize("H,W,lh,lw,l,rho,r", [(48, 40, 12, 10, 16, 4, 1), (37, 45, 10, 12, 16, 4, 1),
-                                              (30, 30, 11, 11, 8, 3, 0), (20, 28, 8, 9, 8, 4, 2)])
+                                              (30, 30, 11, 11, 8, 3, 0), (20, 28, 8, 9, 8, 4, 2),
+                                              (30, 30, 20, 3, 8, 2, 2)])
 def test_corresponding_lr_dense_vs_grouped_and_library(H, W, lh, lw, l, rho, r):
     """Both oracle modes agree and match torch SDPA given the variant's mask;
     the LR window-first order is a bijection grouping LR tokens by window."""
