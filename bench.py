@@ -200,7 +200,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "hr_grid": [w.hr_h, w.hr_w], "lr_grid": [w.lr_h, w.lr_w],
                    "n_text": w.n_text, "heads": w.heads, "head_dim": w.head_dim, "window": w.window,
-                   "radius": w.radius, "rho": w.rho, "batch": w.batch, "seq_len": w.seq_len,
+                   "radius": w.radius, "rho": w.rho, "lr_mode": w.lr_mode, "batch": w.batch, "seq_len": w.seq_len,
                    "pairs_per_head": info["pairs_per_head"], "eff_flop_per_step": flops,
                    "step": "ug_permute_rope(Q,K) + ug_permute(V) + ug_attn_fwd_raster"},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(attn_tflops, 2),

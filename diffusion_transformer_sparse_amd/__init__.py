@@ -5,4 +5,4 @@ include/ultragen.h; all compute runs in the library's HIP kernels."""
 from ._binding import (  # noqa: F401
     EXPORTED, LIB_PATH, UG_BF16, UG_F32, UG_PLAN_HOST_ONLY, Layer, Plan, UgDesc, UgError, UgInfo, desc_of, lib,
     make_desc, ug_attn_fwd, ug_attn_fwd_raster, ug_last_error, ug_permute, ug_permute_rope, ug_plan, ug_plan_export,
-    ug_plan_free, ug_plan_info, ug_rope2d, ug_status_str, ug_unpermute)
+    ug_plan_export_lr, ug_plan_free, ug_plan_info, ug_rope2d, ug_status_str, ug_unpermute)

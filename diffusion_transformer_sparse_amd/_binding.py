@@ -19,7 +19,8 @@ UG_OK, UG_ERR_INVALID_ARGUMENT, UG_ERR_UNSUPPORTED, UG_ERR_OUT_OF_MEMORY, UG_ERR
 UG_F32, UG_BF16 = 0, 1
 UG_PLAN_HOST_ONLY = 1
 
-EXPORTED = ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_permute", "ug_unpermute",
+EXPORTED = ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr", "ug_permute",
+            "ug_unpermute",
             "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_status_str", "ug_last_error")
 
 
@@ -27,7 +28,7 @@ class UgDesc(ctypes.Structure):
     _fields_ = [("batch", c_int32), ("heads", c_int32), ("head_dim", c_int32), ("hr_h", c_int32),
                 ("hr_w", c_int32), ("lr_h", c_int32), ("lr_w", c_int32), ("n_text", c_int32),
                 ("window", c_int32), ("radius", c_int32), ("rho", c_int32), ("dtype", c_int32),
-                ("flags", c_int32), ("reserved", c_int32), ("rope_theta", c_double)]
+                ("flags", c_int32), ("lr_mode", c_int32), ("rope_theta", c_double)]
 
 
 class UgInfo(ctypes.Structure):
@@ -59,6 +60,7 @@ def lib():
         L.ug_plan_free.argtypes = [c_void_p]
         L.ug_plan_info.argtypes = [c_void_p, POINTER(UgInfo)]
         L.ug_plan_export.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.ug_plan_export_lr.argtypes = [c_void_p, c_void_p, c_void_p]
         L.ug_permute.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
         L.ug_unpermute.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
         L.ug_rope2d.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
@@ -69,7 +71,8 @@ def lib():
         L.ug_status_str.restype = c_char_p
         L.ug_last_error.argtypes = []
         L.ug_last_error.restype = c_char_p
-        for name in ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_permute", "ug_unpermute",
+        for name in ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr", "ug_permute",
+                     "ug_unpermute",
                      "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster"):
             getattr(L, name).restype = c_int32
         _lib = L
@@ -94,17 +97,17 @@ def _check(fn, status):
 
 
 def make_desc(hr_h, hr_w, lr_h, lr_w, n_text, heads, head_dim, dtype="bf16", window=16, radius=1, rho=4,
-              rope_theta=10000.0, batch=1, host_only=False) -> UgDesc:
+              rope_theta=10000.0, batch=1, host_only=False, lr_mode=0) -> UgDesc:
     return UgDesc(batch=batch, heads=heads, head_dim=head_dim, hr_h=hr_h, hr_w=hr_w, lr_h=lr_h, lr_w=lr_w,
                   n_text=n_text, window=window, radius=radius, rho=rho,
                   dtype=UG_BF16 if dtype in ("bf16", UG_BF16) else UG_F32,
-                  flags=UG_PLAN_HOST_ONLY if host_only else 0, reserved=0, rope_theta=rope_theta)
+                  flags=UG_PLAN_HOST_ONLY if host_only else 0, lr_mode=lr_mode, rope_theta=rope_theta)
 
 
 def desc_of(w, host_only=False) -> UgDesc:
     """Descriptor of a workloads.Workload (duck-typed)."""
     return make_desc(w.hr_h, w.hr_w, w.lr_h, w.lr_w, w.n_text, w.heads, w.head_dim, w.dtype, w.window,
-                     w.radius, w.rho, w.rope_theta, w.batch, host_only)
+                     w.radius, w.rho, w.rope_theta, w.batch, host_only, getattr(w, "lr_mode", 0))
 
 
 class Plan:
@@ -163,6 +166,14 @@ def ug_plan_export(plan: Plan) -> dict:
     _check("ug_plan_export", lib().ug_plan_export(plan.handle, perm.ctypes.data, win_off.ctypes.data,
                                                   nbr.ctypes.data, nbr_off.ctypes.data))
     return {"perm": perm, "win_off": win_off, "nbr": nbr[:info["n_neighbour_entries"]], "nbr_off": nbr_off}
+
+
+def ug_plan_export_lr(plan: Plan) -> dict:
+    info = plan.info
+    lr_perm = np.empty(max(1, info["n_lr"]), np.int32)
+    lr_win_off = np.empty(info["n_windows"] + 2, np.int32)
+    _check("ug_plan_export_lr", lib().ug_plan_export_lr(plan.handle, lr_perm.ctypes.data, lr_win_off.ctypes.data))
+    return {"lr_perm": lr_perm[:info["n_lr"]], "lr_win_off": lr_win_off}
 
 
 # ---------------------------------------------------------------- device calls

@@ -28,9 +28,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
 // Row gather: dst row j <- src row map(j), whole token rows (all heads) at a
-// time.  Rows outside [T, T+N) (text, LR) copy in place; HR row T+i copies
-// from T + table[i].  With table = perm this is the window-first
-// permutation, with table = inverse it is the unpermutation.  Pure HBM
+// time.  Text rows copy in place; HR row T+i copies from T + table[i]; LR
+// row T+N+i copies from T+N+lr_table[i] (in place when lr_table is null).
+// With the forward tables this is the window-first permutation, with the
+// inverse tables the unpermutation.  Pure HBM
 // streaming: every byte is read once and written once, so the accesses are
 // non-temporal 16-byte vectors; each thread owns one 16-byte column of
 // kGatherRows consecutive rows and has all of them in flight at once.
@@ -40,7 +41,8 @@ constexpr int kGatherRows = 4;  // token rows per workgroup
 
 __global__ __launch_bounds__(1024) void row_gather_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                           int32_t L, int32_t T, int32_t N, int32_t units,
-                                                          const int32_t* __restrict__ table) {
+                                                          const int32_t* __restrict__ table,
+                                                          const int32_t* __restrict__ lr_table) {
   const int64_t batch_units = int64_t(L) * units;
   src += blockIdx.y * batch_units;
   dst += blockIdx.y * batch_units;
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(1024) void row_gather_kernel(const u32x4* __restric
     for (int r = 0; r < kGatherRows; ++r) {
       const int32_t j = row0 + r;
       if (j < L) {
-        const int32_t s = (j >= T && j < T + N) ? T + table[j - T] : j;
+        const int32_t s = (j < T) ? j : (j < T + N) ? T + table[j - T] : lr_table ? T + N + lr_table[j - T - N] : j;
         v[r] = __builtin_nontemporal_load(src + int64_t(s) * units + c);
       }
     }
@@ -79,6 +81,7 @@ template <typename T>
 __global__ __launch_bounds__(1024) void rope2d_kernel(T* __restrict__ q, T* __restrict__ k, int32_t L, int32_t T0,
                                                       int32_t N, int32_t W, int32_t lr_w, int32_t rho, int32_t heads,
                                                       int32_t D, const int32_t* __restrict__ perm,
+                                                      const int32_t* __restrict__ lr_perm,
                                                       const float2* __restrict__ cs) {
   constexpr int E = 16 / sizeof(T);  // elements per 16-byte vector (8 bf16 or 4 fp32)
   const int32_t units_per_head = D / E;
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(1024) void rope2d_kernel(T* __restrict__ q, T* __re
       pr[r] = idx / W;
       pc[r] = idx - pr[r] * W;
     } else {
-      const int32_t i = rr - N;
+      const int32_t i = lr_perm ? lr_perm[rr - N] : rr - N;  // raster LR index
       const int32_t m = i / lr_w;
       pr[r] = rho * m;
       pc[r] = rho * (i - m * lr_w);
@@ -170,6 +173,7 @@ __global__ __launch_bounds__(1024) void permute_rope_kernel(const T* __restrict_
                                                             int32_t T0, int32_t N, int32_t W, int32_t lr_w,
                                                             int32_t rho, int32_t heads, int32_t D,
                                                             const int32_t* __restrict__ perm,
+                                                            const int32_t* __restrict__ lr_perm,
                                                             const float2* __restrict__ cs) {
   constexpr int E = 16 / sizeof(T);
   const int32_t units_per_head = D / E;
@@ -193,7 +197,8 @@ __global__ __launch_bounds__(1024) void permute_rope_kernel(const T* __restrict_
       pr[r] = idx / W;
       pc[r] = idx - pr[r] * W;
     } else if (j >= T0 + N) {
-      const int32_t i = j - T0 - N;
+      const int32_t i = lr_perm ? lr_perm[j - T0 - N] : j - T0 - N;  // raster LR index
+      src[r] = T0 + N + i;
       const int32_t m = i / lr_w;
       pr[r] = rho * m;
       pc[r] = rho * (i - m * lr_w);
@@ -308,7 +313,8 @@ struct AttnParams {
   const ug::Block* blocks;
   float scale_log2;      // log2(e) / sqrt(D)
   int32_t T, N;          // text rows, HR rows
-  const int32_t* out_perm;  // non-null: write HR output row T+i to raster row T+out_perm[i]
+  const int32_t* out_perm;     // non-null: write HR output row T+i to raster row T+out_perm[i]
+  const int32_t* out_lr_perm;  // non-null (with out_perm): LR row T+N+i to T+N+out_lr_perm[i]
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -706,7 +712,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
     const uint4 val = *reinterpret_cast<const uint4*>(ost + r * RB + ((cc ^ Lds::k_swz(r)) * 16));
     const int32_t row = task.q0 + wave * 32 + r;
     if (row < task.q1) {
-      const int32_t orow = (p.out_perm && row >= p.T && row < p.T + p.N) ? p.T + p.out_perm[row - p.T] : row;
+      int32_t orow = row;
+      if (p.out_perm && row >= p.T) {
+        if (row < p.T + p.N)
+          orow = p.T + p.out_perm[row - p.T];
+        else if (p.out_lr_perm)
+          orow = p.T + p.N + p.out_lr_perm[row - p.T - p.N];
+      }
       *reinterpret_cast<uint4*>(og + orow * rs + cc * Lds::kEl16) = val;
     }
   }
@@ -747,7 +759,8 @@ int current_device() {
   return d;
 }
 
-ug_status gather(ug_plan_t p, const void* src, void* dst, const int32_t* table, hipStream_t s, const char* fn) {
+ug_status gather(ug_plan_t p, const void* src, void* dst, const int32_t* table, const int32_t* lr_table,
+                 hipStream_t s, const char* fn) {
   ug::clear_error();
   ug_status st = check_plan(p, fn);
   if (st != UG_OK) return st;
@@ -762,7 +775,7 @@ ug_status gather(ug_plan_t p, const void* src, void* dst, const int32_t* table, 
   const dim3 grid(unsigned((p->L + kGatherRows - 1) / kGatherRows), unsigned(p->d.batch));
   const unsigned threads = unsigned(std::min<int64_t>(1024, (int64_t(units) + 63) / 64 * 64));
   hipLaunchKernelGGL(row_gather_kernel, grid, dim3(threads), 0, s, static_cast<const u32x4*>(src),
-                     static_cast<u32x4*>(dst), int32_t(p->L), int32_t(p->T), int32_t(p->N), units, table);
+                     static_cast<u32x4*>(dst), int32_t(p->L), int32_t(p->T), int32_t(p->N), units, table, lr_table);
   return launch_status(fn);
 }
 
@@ -801,6 +814,7 @@ ug_status attn_common(ug_plan_t p, const void* q, const void* k, const void* v, 
   ap.T = int32_t(p->T);
   ap.N = int32_t(p->N);
   ap.out_perm = raster_out ? p->d_perm : nullptr;
+  ap.out_lr_perm = raster_out ? p->d_lr_perm : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = p->d.dtype == UG_BF16;
   if (bf && p->d.head_dim == 128)
@@ -819,11 +833,13 @@ ug_status attn_common(ug_plan_t p, const void* q, const void* k, const void* v, 
 extern "C" {
 
 ug_status ug_permute(ug_plan_t p, const void* x_raster, void* x_perm, void* stream) {
-  return gather(p, x_raster, x_perm, p ? p->d_perm : nullptr, static_cast<hipStream_t>(stream), "ug_permute");
+  return gather(p, x_raster, x_perm, p ? p->d_perm : nullptr, p ? p->d_lr_perm : nullptr,
+                static_cast<hipStream_t>(stream), "ug_permute");
 }
 
 ug_status ug_unpermute(ug_plan_t p, const void* x_perm, void* x_raster, void* stream) {
-  return gather(p, x_perm, x_raster, p ? p->d_inv : nullptr, static_cast<hipStream_t>(stream), "ug_unpermute");
+  return gather(p, x_perm, x_raster, p ? p->d_inv : nullptr, p ? p->d_lr_inv : nullptr,
+                static_cast<hipStream_t>(stream), "ug_unpermute");
 }
 
 ug_status ug_rope2d(ug_plan_t p, void* q_perm, void* k_perm, void* stream) {
@@ -849,11 +865,11 @@ ug_status ug_rope2d(ug_plan_t p, void* q_perm, void* k_perm, void* stream) {
   if (p->d.dtype == UG_BF16)
     hipLaunchKernelGGL(rope2d_kernel<__bf16>, grid, dim3(threads), 0, s, static_cast<__bf16*>(q_perm),
                        static_cast<__bf16*>(k_perm), int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w,
-                       p->d.rho, p->d.heads, p->d.head_dim, p->d_perm, cs);
+                       p->d.rho, p->d.heads, p->d.head_dim, p->d_perm, p->d_lr_perm, cs);
   else
     hipLaunchKernelGGL(rope2d_kernel<float>, grid, dim3(threads), 0, s, static_cast<float*>(q_perm),
                        static_cast<float*>(k_perm), int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w,
-                       p->d.rho, p->d.heads, p->d.head_dim, p->d_perm, cs);
+                       p->d.rho, p->d.heads, p->d.head_dim, p->d_perm, p->d_lr_perm, cs);
   return launch_status("ug_rope2d");
 }
 
@@ -896,12 +912,12 @@ ug_status ug_permute_rope(ug_plan_t p, const void* q_raster, const void* k_raste
     hipLaunchKernelGGL(permute_rope_kernel<__bf16>, grid, dim3(threads), 0, s, static_cast<const __bf16*>(q_raster),
                        static_cast<const __bf16*>(k_raster), static_cast<__bf16*>(q_perm),
                        static_cast<__bf16*>(k_perm), int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w,
-                       p->d.rho, p->d.heads, p->d.head_dim, p->d_perm, cs);
+                       p->d.rho, p->d.heads, p->d.head_dim, p->d_perm, p->d_lr_perm, cs);
   else
     hipLaunchKernelGGL(permute_rope_kernel<float>, grid, dim3(threads), 0, s, static_cast<const float*>(q_raster),
                        static_cast<const float*>(k_raster), static_cast<float*>(q_perm), static_cast<float*>(k_perm),
                        int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w, p->d.rho, p->d.heads,
-                       p->d.head_dim, p->d_perm, cs);
+                       p->d.head_dim, p->d_perm, p->d_lr_perm, cs);
   return launch_status("ug_permute_rope");
 }
 

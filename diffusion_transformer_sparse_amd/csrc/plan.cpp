@@ -57,6 +57,7 @@ ug_status validate(const ug_desc* d) {
     return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: rope_theta must be finite and > 0");
   if (d->dtype != UG_F32 && d->dtype != UG_BF16) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: unknown dtype");
   if (d->flags & ~UG_PLAN_HOST_ONLY) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: unknown flags");
+  if (d->lr_mode != 0 && d->lr_mode != 1) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: lr_mode must be 0 or 1");
   const int64_t N = int64_t(d->hr_h) * d->hr_w;
   const int64_t Nlr = int64_t(d->lr_h) * d->lr_w;
   const int64_t L = int64_t(d->n_text) + N + Nlr;
@@ -118,6 +119,38 @@ void build_windows(ug_plan_s& p) {
   p.nbr_off[p.nwin] = int32_t(p.nbr.size());
 }
 
+// LR anchors by window (关键设计 2, "corresponding" anchors): LR token
+// (m, n) sits at (rho*m, rho*n) and belongs to the window containing that
+// position.  Window-first order of the LR grid: windows row-major, tokens
+// row-major inside; tokens outside the window grid last, in raster order.
+// With lr_mode 0 the LR rows keep the raster order (identity).
+void build_lr_windows(ug_plan_s& p) {
+  const int lh = p.d.lr_h, lw = p.d.lr_w, l = p.d.window, rho = p.d.rho;
+  const int64_t nl = p.Nlr;
+  std::vector<int64_t> count(size_t(p.nwin) + 1, 0);  // last bucket: outside the grid
+  auto win_of = [&](int m, int n) -> int64_t {
+    const int64_t a = int64_t(rho) * m / l, b = int64_t(rho) * n / l;
+    return (a < p.gy && b < p.gx) ? a * p.gx + b : int64_t(p.nwin);
+  };
+  for (int m = 0; m < lh; ++m)
+    for (int n = 0; n < lw; ++n) ++count[size_t(win_of(m, n))];
+  p.lr_win_off.assign(size_t(p.nwin) + 2, 0);
+  for (int w = 0; w <= p.nwin; ++w) p.lr_win_off[w + 1] = p.lr_win_off[w] + int32_t(count[w]);
+  p.lr_perm.resize(nl);
+  p.lr_inv.resize(nl);
+  if (p.d.lr_mode == 0) {
+    for (int64_t i = 0; i < nl; ++i) p.lr_perm[i] = p.lr_inv[i] = int32_t(i);
+    return;
+  }
+  std::vector<int32_t> fill(p.lr_win_off.begin(), p.lr_win_off.end() - 1);
+  for (int m = 0; m < lh; ++m)
+    for (int n = 0; n < lw; ++n) {
+      const int32_t slot = fill[size_t(win_of(m, n))]++;
+      p.lr_perm[slot] = m * lw + n;
+      p.lr_inv[m * lw + n] = slot;
+    }
+}
+
 // RoPE table, double precision rounded to float: cs[pos][k] = (cos, sin) of
 // pos * theta^(-2k/(D/2)), k < D/4.
 void build_rope(ug_plan_s& p) {
@@ -157,7 +190,8 @@ int64_t tiles_of(const ug_plan_s& p, const ug::Task& t) {
 
 // Query tiles and their key ranges (the composite mask of 关键设计 2):
 //  text rows -> text + HR; LR rows -> text + LR;
-//  HR rows of window w -> text + neighbouring windows + LR.
+//  HR rows of window w -> text + neighbouring windows + LR (all of it, or with
+//  lr_mode 1 the LR anchors of the neighbouring windows).
 void build_tasks(ug_plan_s& p) {
   const int32_t T = int32_t(p.T), N = int32_t(p.N), L = int32_t(p.L);
   const int QT = ug::kAttnQueryTile;
@@ -178,7 +212,12 @@ void build_tasks(ug_plan_s& p) {
       const int v = p.nbr[e];
       rs.push_back({T + p.win_off[v], T + p.win_off[v + 1]});
     }
-    if (p.Nlr > 0) rs.push_back({T + N, L});
+    if (p.Nlr > 0 && p.d.lr_mode == 0) rs.push_back({T + N, L});
+    if (p.Nlr > 0 && p.d.lr_mode == 1)
+      for (int e = p.nbr_off[w]; e < p.nbr_off[w + 1]; ++e) {
+        const int v = p.nbr[e];
+        rs.push_back({T + N + p.lr_win_off[v], T + N + p.lr_win_off[v + 1]});
+      }
     add_rows(T + p.win_off[w], T + p.win_off[w + 1], rs);
   }
   p.pairs = 0;
@@ -256,10 +295,11 @@ ug_status upload(const std::vector<T>& h, T** d) {
 }
 
 void free_device(ug_plan_s* p) {
-  void* ptrs[] = {p->d_perm, p->d_inv, p->d_rope, p->d_tasks, p->d_ranges, p->d_blocks};
+  void* ptrs[] = {p->d_perm, p->d_inv, p->d_lr_perm, p->d_lr_inv, p->d_rope, p->d_tasks, p->d_ranges, p->d_blocks};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
   p->d_perm = p->d_inv = nullptr;
+  p->d_lr_perm = p->d_lr_inv = nullptr;
   p->d_rope = nullptr;
   p->d_tasks = nullptr;
   p->d_ranges = nullptr;
@@ -304,6 +344,7 @@ ug_status ug_plan(const ug_desc* desc, ug_plan_t* out) {
     p->Nlr = int64_t(desc->lr_h) * desc->lr_w;
     p->L = p->T + p->N + p->Nlr;
     ug::build_windows(*p);
+    ug::build_lr_windows(*p);
     ug::build_rope(*p);
     ug::build_tasks(*p);
     ug::build_blocks(*p);
@@ -318,6 +359,8 @@ ug_status ug_plan(const ug_desc* desc, ug_plan_t* out) {
     s = ug::check_device(p);
     if (s == UG_OK) s = ug::upload(p->perm, &p->d_perm);
     if (s == UG_OK) s = ug::upload(p->inv, &p->d_inv);
+    if (s == UG_OK && p->d.lr_mode == 1) s = ug::upload(p->lr_perm, &p->d_lr_perm);
+    if (s == UG_OK && p->d.lr_mode == 1) s = ug::upload(p->lr_inv, &p->d_lr_inv);
     if (s == UG_OK) s = ug::upload(p->rope_cs, &p->d_rope);
     if (s == UG_OK) s = ug::upload(p->tasks, &p->d_tasks);
     if (s == UG_OK) s = ug::upload(p->ranges, &p->d_ranges);
@@ -370,6 +413,14 @@ ug_status ug_plan_export(ug_plan_t p, int32_t* perm, int32_t* win_off, int32_t* 
   if (win_off) std::memcpy(win_off, p->win_off.data(), p->win_off.size() * sizeof(int32_t));
   if (nbr && !p->nbr.empty()) std::memcpy(nbr, p->nbr.data(), p->nbr.size() * sizeof(int32_t));
   if (nbr_off) std::memcpy(nbr_off, p->nbr_off.data(), p->nbr_off.size() * sizeof(int32_t));
+  return UG_OK;
+}
+
+ug_status ug_plan_export_lr(ug_plan_t p, int32_t* lr_perm, int32_t* lr_win_off) {
+  ug::clear_error();
+  if (!p) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_plan_export_lr: plan is NULL");
+  if (lr_perm && !p->lr_perm.empty()) std::memcpy(lr_perm, p->lr_perm.data(), p->lr_perm.size() * sizeof(int32_t));
+  if (lr_win_off) std::memcpy(lr_win_off, p->lr_win_off.data(), p->lr_win_off.size() * sizeof(int32_t));
   return UG_OK;
 }
 

@@ -40,6 +40,8 @@ struct ug_plan_s {
 
   // host tables
   std::vector<int32_t> perm, inv, win_off, nbr, nbr_off;
+  // LR window-first order (lr_mode 1; the identity otherwise) and window offsets
+  std::vector<int32_t> lr_perm, lr_inv, lr_win_off;
   int32_t rope_P = 0;
   std::vector<float> rope_cs;  // [rope_P][D/4][2]: cos, sin of pos * omega_k
   std::vector<ug::Task> tasks;
@@ -52,6 +54,8 @@ struct ug_plan_s {
   // device copies (owned)
   int32_t* d_perm = nullptr;
   int32_t* d_inv = nullptr;
+  int32_t* d_lr_perm = nullptr;  // null unless lr_mode 1
+  int32_t* d_lr_inv = nullptr;
   float* d_rope = nullptr;
   ug::Task* d_tasks = nullptr;
   ug::Range* d_ranges = nullptr;

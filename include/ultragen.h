@@ -22,7 +22,8 @@
  *      permuted layout: HR rows in window-first order (windows row-major,
  *                       tokens row-major inside a window; partial windows at
  *                       the bottom/right edges of a ragged grid, no padding);
- *                       text and LR rows keep their places.
+ *                       text rows keep their places; LR rows keep theirs
+ *                       unless lr_mode = 1 (then window-first as well).
  *  - The caller owns every tensor and the workspace; the plan owns its own
  *    device tables.  No entry point allocates device memory except ug_plan.
  *  - Launches are asynchronous on `stream` (a hipStream_t; NULL = the null
@@ -65,6 +66,13 @@ typedef enum ug_dtype { UG_F32 = 0, UG_BF16 = 1 } ug_dtype;
  *    of more than 256 tokens are split into several query tiles.
  *  - radius: HR queries see HR keys whose window is within Chebyshev
  *    distance `radius` of their own (1 = own + adjacent windows, 3x3).
+ *  - lr_mode: which LR tokens an HR query sees.  0 = all of them (the LR
+ *    latent as one global anchor set, gist.science summary 2.B).  1 = only
+ *    the "corresponding" anchors of 关键设计 2: LR token (m, n) belongs to the
+ *    window containing its scaled position (rho*m, rho*n), and an HR query
+ *    sees the LR tokens of the windows within `radius` of its own.  With
+ *    lr_mode 1 the permuted layout also orders the LR rows window-first (by
+ *    that window, then row-major); LR tokens outside the window grid go last.
  *  - rope_theta: base of the axial RoPE frequencies omega_k =
  *    theta^(-2k/(D/2)); dims [0, D/2) are rotated by the row position,
  *    [D/2, D) by the column position, pairs (2k, 2k+1).
@@ -82,7 +90,7 @@ typedef struct ug_desc {
   int32_t rho;
   int32_t dtype; /* ug_dtype */
   int32_t flags; /* UG_PLAN_* */
-  int32_t reserved;
+  int32_t lr_mode; /* 0: HR queries see all LR tokens; 1: corresponding LR only */
   double rope_theta;
 } ug_desc;
 
@@ -132,6 +140,18 @@ ug_status ug_plan_export(ug_plan_t plan, int32_t* perm, int32_t* win_off, int32_
                          int32_t* nbr_off);
 
 /*
+ * ug_plan_export_lr: the LR tables (either pointer may be NULL).
+ *  lr_perm    int32[n_lr]           raster LR index held by LR slot i of the
+ *                                   permuted layout (the identity when
+ *                                   lr_mode = 0)
+ *  lr_win_off int32[n_windows + 2]  LR slots [lr_win_off[w], lr_win_off[w+1])
+ *                                   hold window w's anchors (lr_mode = 1
+ *                                   order); entries n_windows .. n_windows+1
+ *                                   bound the out-of-grid tail
+ */
+ug_status ug_plan_export_lr(ug_plan_t plan, int32_t* lr_perm, int32_t* lr_win_off);
+
+/*
  * ug_permute: x_perm = x_raster with HR rows gathered into window-first
  * order (关键设计 1; gist.science summary 2.A, window-first token
  * permutation); text and LR rows copied unchanged.  Out of place:
@@ -153,8 +173,9 @@ ug_status ug_rope2d(ug_plan_t plan, void* q_perm, void* k_perm, void* stream);
  * ug_attn_fwd: O = softmax(Q K^T / sqrt(D) + M) V per (batch, head) on
  * permuted, rotated Q and K and permuted V (关键设计 3's joint attention over
  * [C_T; X; X_lr]).  M is the composite mask of 关键设计 2: a text query sees
- * text and HR keys; an HR query sees text, all LR, and the HR keys of its own
- * and adjacent windows; an LR query sees LR and text.  Masked keys are
+ * text and HR keys; an HR query sees text, the HR keys of its own and
+ * adjacent windows, and all LR keys (lr_mode 0) or the LR anchors of those
+ * same windows (lr_mode 1); an LR query sees LR and text.  Masked keys are
  * excluded (additive -inf).  O is written in the permuted layout.  bf16: bf16
  * MFMA products, fp32 softmax and accumulation, O rounded to nearest even;
  * fp32: fp32 MFMA throughout.  `workspace` may be NULL when

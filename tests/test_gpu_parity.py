@@ -15,6 +15,8 @@ from tests.gpu_util import (assert_close, qkv_device, seg_errors, to_device, to_
 pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny", "tiny_masked", "small_ragged", "small_d64", "small_ragged_f32", "1k"]
+# corresponding-LR variant (lr_mode 1): LR rows permuted window-first too
+CORR = ["tiny_masked_corr", "small_ragged_corr", "ragged_corr_f32"]
 
 
 @pytest.fixture(scope="module")
@@ -29,18 +31,24 @@ def plan_of(U, w):
     return U.ug_plan(U.desc_of(w))
 
 
+def permuted_order(w):
+    """Raster row held by each row of the permuted layout, from the oracle's
+    window-first orders (HR always; LR when lr_mode is 1)."""
+    T, N = w.n_text, w.n_hr
+    perm = O.window_first_perm(w.hr_h, w.hr_w, w.window)
+    lr = O.lr_window_first_perm(O.geometry_of(w)) if w.lr_mode == 1 else np.arange(w.n_lr)
+    return np.concatenate([np.arange(T), T + perm, T + N + lr]).astype(np.int64)
+
+
 def expected_permuted(w, x):
     """Host gather with the oracle's window-first order (rows of all heads)."""
-    perm = O.window_first_perm(w.hr_h, w.hr_w, w.window)
-    T, N = w.n_text, w.n_hr
-    out = x.copy()
-    out[:, T:T + N] = x[:, T + perm]
-    return out
+    return x[:, permuted_order(w)]
 
 
 # ------------------------------------------------------------------ permutation
 
-@pytest.mark.parametrize("name", ["tiny", "small_ragged", "small_ragged_f32", "1k", "ragged", "4k"])
+@pytest.mark.parametrize("name", ["tiny", "small_ragged", "small_ragged_f32", "1k", "ragged", "4k",
+                                  "small_ragged_corr", "ragged_corr_f32", "4k_corr"])
 def test_permute_unpermute_bit_exact(U, name):
     import torch
     w = WL.WORKLOADS[name]
@@ -56,7 +64,7 @@ def test_permute_unpermute_bit_exact(U, name):
 
 # ------------------------------------------------------------------ RoPE
 
-@pytest.mark.parametrize("name", ["tiny", "small_ragged", "small_d64", "small_ragged_f32", "1k"])
+@pytest.mark.parametrize("name", ["tiny", "small_ragged", "small_d64", "small_ragged_f32", "1k"] + CORR)
 def test_rope2d_matches_oracle(U, name):
     import torch
     w = WL.WORKLOADS[name]
@@ -68,9 +76,7 @@ def test_rope2d_matches_oracle(U, name):
     torch.cuda.synchronize()
     assert torch.equal(qp[:, :w.n_text], text_before)
     geo = O.geometry_of(w)
-    perm = O.window_first_perm(w.hr_h, w.hr_w, w.window)
-    T, N = w.n_text, w.n_hr
-    order = np.concatenate([np.arange(T), T + perm, np.arange(T + N, w.seq_len)])
+    order = permuted_order(w)
     for t, dev in ((WL.Q, qp), (WL.K, kp)):
         got = to_host_f64(dev, w.dtype)[0]
         for h in range(w.heads):
@@ -100,8 +106,9 @@ def oracle_attn_only(w, h):
     return O.attention_grouped(geo, WL.head_f64(w, WL.Q, h), WL.head_f64(w, WL.K, h), WL.head_f64(w, WL.V, h))
 
 
-@pytest.mark.parametrize("name,qscale", [(n, 1.0) for n in SMALL] + [("small_ragged", 8.0), ("1k", 8.0),
-                                                                    ("tiny_masked", 8.0)])
+@pytest.mark.parametrize("name,qscale", [(n, 1.0) for n in SMALL + CORR] + [("small_ragged", 8.0), ("1k", 8.0),
+                                                                           ("tiny_masked", 8.0),
+                                                                           ("small_ragged_corr", 8.0)])
 def test_attention_matches_oracle(U, name, qscale):
     w = WL.WORKLOADS[name].with_(q_scale=qscale)
     got = run_attn_only(U, w)
@@ -110,7 +117,7 @@ def test_attention_matches_oracle(U, name, qscale):
 
 
 @pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("name", SMALL + CORR)
 def test_full_layer_matches_oracle(U, name, fused):
     import torch
     w = WL.WORKLOADS[name]
@@ -140,7 +147,7 @@ def sample_rows(w, seed=0):
 
 
 @pytest.mark.parametrize("name,fused", [("2k", True), ("ragged", True), ("4k", True), ("4k", False),
-                                        ("8k", True)])
+                                        ("8k", True), ("4k_corr", True), ("4k_corr", False)])
 def test_full_size_sampled_rows(U, name, fused):
     """The bench's launch configuration (fused layer) at full size; the
     oracle recomputes sampled rows one by one (text, corner/edge/interior HR
@@ -161,7 +168,7 @@ def test_full_size_sampled_rows(U, name, fused):
     assert torch.isfinite(out.float()).all()
 
 
-@pytest.mark.parametrize("name", ["tiny", "small_ragged", "small_d64", "small_ragged_f32", "1k", "ragged"])
+@pytest.mark.parametrize("name", ["tiny", "small_ragged", "small_d64", "small_ragged_f32", "1k", "ragged"] + CORR)
 def test_fused_entry_points_bit_exact(U, name):
     """ug_permute_rope == ug_permute + ug_rope2d and ug_attn_fwd_raster ==
     ug_attn_fwd + ug_unpermute, bit for bit."""
@@ -204,7 +211,13 @@ EDGE = {
     "window_covers_grid": dict(window=64),
     "batch2": dict(batch=2),
     "one_text": dict(n_text=1),
+    "corr_radius0": dict(lr_mode=1, radius=0),
+    "corr_window8_rho3": dict(lr_mode=1, window=8, rho=3),   # windows with 0..9 anchors
+    "corr_lr_overhang": dict(lr_mode=1, lr_h=14, lr_w=14),   # anchors past the window grid
+    "corr_no_text": dict(lr_mode=1, n_text=0),
+    "corr_batch2": dict(lr_mode=1, batch=2),
 }
+FUSED_EDGE = ("batch2", "no_lr", "corr_batch2", "corr_lr_overhang")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -216,7 +229,7 @@ def test_edge_cases(U, case, dtype):
     p = plan_of(U, w)
     q, k, v = qkv_device(w)
     out = torch.empty_like(q)
-    U.Layer(p, fused=(case in ("batch2", "no_lr")))(q, k, v, out)
+    U.Layer(p, fused=(case in FUSED_EDGE))(q, k, v, out)
     torch.cuda.synchronize()
     geo = O.geometry_of(w)
     for b in range(w.batch):

@@ -53,7 +53,30 @@ def test_plan_tables_bit_exact(name):
     assert info["pairs_per_head"] == O.pair_count(geo)
     assert info["seq_len"] == geo.seq_len and info["n_lr"] == geo.n_lr
     assert info["eff_flops"] == 4.0 * w.head_dim * info["pairs_per_head"] * w.heads * w.batch
+    lr = U.ug_plan_export_lr(p)
+    if w.lr_mode == 1:
+        assert np.array_equal(lr["lr_perm"], O.lr_window_first_perm(geo))
+        assert np.array_equal(lr["lr_win_off"], O.lr_window_offsets(geo))
+    else:
+        assert np.array_equal(lr["lr_perm"], np.arange(w.n_lr))
     p.close()
+
+
+@pytest.mark.parametrize("H,W,l,r,T,lh,lw,rho", [(3, 5, 2, 1, 2, 1, 2, 2), (17, 33, 16, 1, 0, 5, 9, 4),
+                                                  (64, 48, 32, 1, 5, 16, 12, 4), (20, 20, 64, 0, 3, 5, 5, 4),
+                                                  (33, 65, 16, 0, 0, 9, 17, 4), (8, 8, 4, 1, 1, 4, 4, 2),
+                                                  (30, 30, 8, 2, 4, 20, 3, 2), (16, 16, 16, 1, 2, 1, 1, 1)])
+def test_corresponding_lr_tables(H, W, l, r, T, lh, lw, rho):
+    """lr_mode 1: LR window-first order, LR window offsets and the exact pair
+    count (hence the key ranges) agree with the oracle, also where LR
+    anchors overhang the window grid."""
+    d = U.make_desc(H, W, lh, lw, T, 2, 64, "f32", window=l, radius=r, rho=rho, host_only=True, lr_mode=1)
+    p = U.ug_plan(d)
+    geo = O.Geometry(H, W, lh, lw, T, l, r, rho, lr_mode=1)
+    lr = U.ug_plan_export_lr(p)
+    assert np.array_equal(lr["lr_perm"], O.lr_window_first_perm(geo))
+    assert np.array_equal(lr["lr_win_off"], O.lr_window_offsets(geo))
+    assert p.info["pairs_per_head"] == O.pair_count(geo) == int(O.allowed_dense(geo).sum())
 
 
 @pytest.mark.parametrize("H,W,l,r,T,lh,lw", [(3, 5, 2, 1, 2, 1, 2), (17, 33, 16, 1, 0, 5, 9), (40, 40, 8, 2, 7, 0, 0),
@@ -83,7 +106,8 @@ def test_rope_table_rows_cover_scaled_lr_positions():
 @pytest.mark.parametrize("field,value,status", [
     ("batch", 0, U.UgError), ("heads", 0, U.UgError), ("head_dim", 6, U.UgError), ("hr_h", 0, U.UgError),
     ("lr_w", -1, U.UgError), ("n_text", -3, U.UgError), ("window", 0, U.UgError), ("radius", -1, U.UgError),
-    ("rho", 0, U.UgError), ("dtype", 7, U.UgError), ("flags", 8, U.UgError), ("rope_theta", -1.0, U.UgError)])
+    ("rho", 0, U.UgError), ("dtype", 7, U.UgError), ("flags", 8, U.UgError), ("rope_theta", -1.0, U.UgError),
+    ("lr_mode", 2, U.UgError), ("lr_mode", -1, U.UgError)])
 def test_descriptor_validation(field, value, status):
     d = U.desc_of(WORKLOADS["tiny"], host_only=True)
     setattr(d, field, value)

@@ -46,6 +46,7 @@ class Workload:
     rope_theta: float = 10000.0
     batch: int = 1
     q_scale: float = 1.0  # power of two; 8 gives peaked softmax rows
+    lr_mode: int = 0      # 0: HR queries see every LR token; 1: corresponding LR windows only
 
     @property
     def n_hr(self) -> int:
@@ -87,6 +88,13 @@ WORKLOADS = {
     "small_ragged": Workload("small_ragged", 7, 40, 56, 10, 14, 40, 3, 128, "bf16"),
     "small_d64": Workload("small_d64", 8, 48, 40, 12, 10, 24, 2, 64, "bf16"),
     "small_ragged_f32": Workload("small_ragged_f32", 9, 37, 45, 10, 12, 9, 2, 64, "f32"),
+    # corresponding-LR variant (each HR window sees the LR anchors of its
+    # neighbourhood only); LR grids that overhang the HR grid put anchors
+    # outside every window
+    "4k_corr": Workload("4k_corr", 10, 256, 256, 64, 64, 512, 24, 128, "bf16", lr_mode=1),
+    "small_ragged_corr": Workload("small_ragged_corr", 11, 40, 56, 10, 14, 40, 3, 128, "bf16", lr_mode=1),
+    "tiny_masked_corr": Workload("tiny_masked_corr", 12, 48, 48, 12, 12, 16, 2, 64, "f32", lr_mode=1),
+    "ragged_corr_f32": Workload("ragged_corr_f32", 13, 37, 45, 11, 13, 9, 2, 64, "f32", lr_mode=1),
 }
 
 
