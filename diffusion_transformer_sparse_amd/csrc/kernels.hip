@@ -467,12 +467,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
   const int32_t qload = qrow < task.q1 ? qrow : task.q1 - 1;
   const float c2 = p.scale_log2;
 
-  // number of 64-key tiles
-  int32_t ntiles = 0;
-  for (int32_t r = task.r0; r < task.r1; ++r) {
-    const ug::Range rg = p.ranges[r];
-    ntiles += (rg.k1 - rg.k0 + kKT - 1) / kKT;
-  }
+  // The task's key ranges (at most ug::kAttnMaxRanges, checked at launch)
+  // are staged in LDS, so moving to the next range inside the tile loop is an
+  // LDS read rather than a global load that would wait on the tile loads in
+  // flight.
+  __shared__ ug::Range s_rng[ug::kAttnMaxRanges];
+  const int32_t nr = task.r1 - task.r0;
+  if (tid < nr) s_rng[tid] = p.ranges[task.r0 + tid];
 
   // The wave's queries as the B operand of S^T = K Q^T.
   constexpr int kQRegs = kBF ? D / 16 : D / 2;
@@ -484,6 +485,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
       qf[i] = *reinterpret_cast<const bf16x8*>(qg + qload * rs + 16 * i + 8 * g);
     else
       qf[i] = qg[qload * rs + 2 * i + g];
+  }
+  __syncthreads();  // s_rng is filled
+
+  // number of 64-key tiles
+  int32_t ntiles = 0;
+  for (int32_t r = 0; r < nr; ++r) {
+    const ug::Range rg = s_rng[r];
+    ntiles += (rg.k1 - rg.k0 + kKT - 1) / kKT;
   }
 
   // Per-lane LDS byte offsets.  K operand of step i: row l32 (plus 32 per
@@ -518,7 +527,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
   float lsum = 0.f;      // this lane half's share of the row sum
 
   TileCursor ck, cv;  // next K tile to load, next V tile to load
-  ck.init(p.ranges, task.r0, task.r1);
+  ck.init(s_rng, 0, nr);
   cv = ck;
   TileLoader<T, D, false> kld;
   TileLoader<T, D, true> vld;
@@ -562,11 +571,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
   kld.issue(kg, rs, ck.ks, ck.nv(), smem, tid, wave);
   vld.issue(vg, rs, cv.ks, cv.nv(), smem + 2 * TB, tid, wave);
   const int32_t nv_cur = cv.nv();
-  ck.advance(p.ranges);
-  cv.advance(p.ranges);
+  ck.advance(s_rng);
+  cv.advance(s_rng);
   if (ntiles > 1) {
     kld.issue(kg, rs, ck.ks, ck.nv(), smem + TB, tid, wave);
-    ck.advance(p.ranges);
+    ck.advance(s_rng);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -591,11 +600,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
     const int32_t nv_next = has_v ? cv.nv() : kKT;
     if (has_k) {  // K_{i+2} replaces K_i
       kld.issue(kg, rs, ck.ks, ck.nv(), smem + (PAR ? TB : 0), tid, wave);
-      ck.advance(p.ranges);
+      ck.advance(s_rng);
     }
     if (has_v) {  // V_{i+1} replaces V_{i-1}
       vld.issue(vg, rs, cv.ks, nv_next, smem + 2 * TB + (PAR ? 0 : TB), tid, wave);
-      cv.advance(p.ranges);
+      cv.advance(s_rng);
     }
 
     if constexpr (kBF) {
@@ -705,22 +714,34 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
   // each wave reads back only its own block: LDS operations of one wave
   // complete in order, so no barrier is needed between the write and read.
   constexpr int rows_per_pass = 64 / Lds::kChunks;
+  constexpr int kPasses = 32 / rows_per_pass;
+  // Destination rows first, as branch-free table reads (rows past the tile
+  // are clamped for the lookup and skipped at the store), so that all the
+  // lookups are in flight together.
+  int32_t orow[kPasses];
+  if (p.out_perm) {  // uniform
 #pragma unroll
-  for (int pass = 0; pass < 32 / rows_per_pass; ++pass) {
+    for (int pass = 0; pass < kPasses; ++pass) {
+      const int32_t row = min(task.q0 + wave * 32 + pass * rows_per_pass + lane / Lds::kChunks, task.q1 - 1);
+      const bool hr = row >= p.T && row < p.T + p.N;
+      const bool lr = row >= p.T + p.N && p.out_lr_perm != nullptr;
+      const int32_t* tab = lr ? p.out_lr_perm : p.out_perm;
+      const int32_t idx = hr ? row - p.T : lr ? row - p.T - p.N : 0;
+      const int32_t v = tab[idx];
+      orow[pass] = hr ? p.T + v : lr ? p.T + p.N + v : row;
+    }
+  } else {
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass)
+      orow[pass] = task.q0 + wave * 32 + pass * rows_per_pass + lane / Lds::kChunks;
+  }
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
     const int r = pass * rows_per_pass + lane / Lds::kChunks;
     const int cc = lane % Lds::kChunks;
     const uint4 val = *reinterpret_cast<const uint4*>(ost + r * RB + ((cc ^ Lds::k_swz(r)) * 16));
-    const int32_t row = task.q0 + wave * 32 + r;
-    if (row < task.q1) {
-      int32_t orow = row;
-      if (p.out_perm && row >= p.T) {
-        if (row < p.T + p.N)
-          orow = p.T + p.out_perm[row - p.T];
-        else if (p.out_lr_perm)
-          orow = p.T + p.N + p.out_lr_perm[row - p.T - p.N];
-      }
-      *reinterpret_cast<uint4*>(og + orow * rs + cc * Lds::kEl16) = val;
-    }
+    if (task.q0 + wave * 32 + r < task.q1)
+      *reinterpret_cast<uint4*>(og + int64_t(orow[pass]) * rs + cc * Lds::kEl16) = val;
   }
 }
 
@@ -798,6 +819,10 @@ ug_status attn_common(ug_plan_t p, const void* q, const void* k, const void* v, 
     return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": o overlaps q, k or v");
   if (current_device() != p->device)
     return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": current device is not the plan's device");
+  if (p->max_task_ranges > ug::kAttnMaxRanges)
+    return ug::fail(UG_ERR_UNSUPPORTED, std::string(fn) + ": a query tile has " + std::to_string(p->max_task_ranges) +
+                                            " key ranges, more than the kernel stages (" +
+                                            std::to_string(ug::kAttnMaxRanges) + "); use a smaller radius");
   if (p->blocks.empty()) return UG_OK;
   AttnParams ap{};
   ap.q = q;

@@ -222,7 +222,9 @@ void build_tasks(ug_plan_s& p) {
   }
   p.pairs = 0;
   p.key_tiles = 0;
+  p.max_task_ranges = 0;
   for (const auto& t : p.tasks) {
+    p.max_task_ranges = std::max(p.max_task_ranges, t.r1 - t.r0);
     int64_t keys = 0;
     for (int r = t.r0; r < t.r1; ++r) keys += p.ranges[r].k1 - p.ranges[r].k0;
     p.pairs += int64_t(t.q1 - t.q0) * keys;

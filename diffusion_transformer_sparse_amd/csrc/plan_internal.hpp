@@ -28,6 +28,7 @@ struct Block {
 constexpr int kAttnQueryTile = 256;  // query rows per workgroup (8 waves x 32)
 constexpr int kAttnKeyTile = 64;     // key rows per LDS stage
 constexpr int kXcds = 8;             // gfx950: workgroups round-robin over 8 XCDs
+constexpr int kAttnMaxRanges = 64;   // key ranges one query tile may have (staged in LDS)
 
 }  // namespace ug
 
@@ -50,6 +51,7 @@ struct ug_plan_s {
   int64_t pairs = 0;      // allowed (q, k) pairs per (batch, head)
   int64_t key_tiles = 0;  // 64-key tiles per (batch, head)
   int32_t max_nbr = 0;
+  int32_t max_task_ranges = 0;  // most key ranges of any query tile
 
   // device copies (owned)
   int32_t* d_perm = nullptr;
