@@ -19,6 +19,10 @@ Sources (cited by page title and section):
         2.B (Attention Masking): windows attend to themselves and adjacent
         windows and to the scaled global guidance tokens; LR tokens attend
         globally to each other.
+  [KD3-FT] papernotes.org notes, 关键设计 3 and the 损失函数 / 训练策略
+        section: the LR branch is fine-tuned (LoRA on its Q, K, V
+        projections) by gradient descent on the flow-matching loss, so the
+        loss is differentiated through the joint attention.
 
 Everything is computed in float64, in RASTER order (text rows, then HR rows
 r*W + c, then LR rows m*w + n), and every mask decision is taken from 2D
@@ -45,6 +49,11 @@ open (all listed in the design doc's table of readings):
      (only possible when the LR grid is given larger than ceil(H/rho) x
      ceil(W/rho)) is inside no window, so it corresponds to none and no HR
      query sees it; LR queries still see it.
+  R11 backward [KD3-FT]: the pages only say the attention is trained, so the
+     backward is the exact derivative of the forward above (RoPE, composite
+     mask, softmax, PV) with respect to the raster Q, K, V, given dO; the
+     log-sum-exp saved by the forward is the natural log of the softmax
+     denominator of the scaled logits q.k/sqrt(D).
 """
 from __future__ import annotations
 
@@ -365,3 +374,156 @@ def forward_rows(g: Geometry, q, k, v, theta, rows):
         keys = allowed_keys_of(g, coords, int(i))
         out[idx] = _rows_attention(qr, kr, v, np.array([i]), keys)[0]
     return out
+
+
+# --------------------------------------------------------------------------
+# Backward ([KD3-FT], R11): gradients of O = softmax(S) V, S = Qr Kr^T/sqrt(D)
+# over the allowed keys, then of the RoPE rotation.
+# --------------------------------------------------------------------------
+
+def allowed_queries_of(g: Geometry, coords, j: int) -> np.ndarray:
+    """Raster indices of the queries that attend to key row j (the column of
+    the composite mask, written out from coordinates like allowed_keys_of)."""
+    kind, _, _, wy, wx = coords
+    if kind[j] == TEXT:      # text, HR and LR queries all see text keys
+        ok = np.ones(kind.size, bool)
+    elif kind[j] == HR:      # text queries see all HR; HR queries of nearby windows
+        near = np.maximum(np.abs(wy - wy[j]), np.abs(wx - wx[j])) <= g.radius
+        ok = (kind == TEXT) | ((kind == HR) & near)
+    else:                    # HR queries (all, or nearby windows for lr_mode 1) and LR queries
+        if g.lr_mode == 1:
+            near = np.maximum(np.abs(wy - wy[j]), np.abs(wx - wx[j])) <= g.radius
+            inside = bool(_in_window_grid(g, wy[j:j + 1], wx[j:j + 1])[0])
+            hr_ok = (kind == HR) & near & inside
+        else:
+            hr_ok = kind == HR
+        ok = hr_ok | (kind == LR)
+    return np.nonzero(ok)[0]
+
+
+def rope_rotate_transpose(x, pos_r, pos_c, theta):
+    """Transpose of the RoPE rotation (each 2x2 block is orthogonal, so the
+    transpose is the rotation by the negated angle): maps dL/d(rotated x)
+    to dL/dx."""
+    return rope_rotate(x, -np.asarray(pos_r), -np.asarray(pos_c), theta)
+
+
+def _row_stats(qr, kr, v, i, keys):
+    """Softmax row i over `keys`: probabilities, natural-log LSE of the scaled
+    logits, and the output row."""
+    D = qr.shape[1]
+    s = (kr[keys] @ qr[i]) / math.sqrt(D)
+    mx = s.max()
+    e = np.exp(s - mx)
+    z = e.sum()
+    p = e / z
+    return p, mx + math.log(z), p @ v[keys]
+
+
+def lse_grouped(g: Geometry, qr, kr) -> np.ndarray:
+    """Natural-log log-sum-exp of the scaled logits over each row's allowed
+    keys (one head, raster order)."""
+    coords = token_coords(g)
+    D = qr.shape[1]
+    out = np.empty(g.seq_len)
+    for i in range(g.seq_len):
+        keys = allowed_keys_of(g, coords, i)
+        s = (kr[keys] @ qr[i]) / math.sqrt(D)
+        mx = s.max()
+        out[i] = mx + math.log(np.exp(s - mx).sum())
+    return out
+
+
+def attention_backward_grouped(g: Geometry, qr, kr, v, do):
+    """Gradients (dQr, dKr, dV) of the masked attention of one head with
+    respect to the rotated Q, K and to V, given dO (raster order):
+      P = softmax(S) over allowed keys, dP = dO V^T, Delta_i = sum_j P_ij dP_ij,
+      dS = P * (dP - Delta), dQr = dS Kr / sqrt(D), dKr = dS^T Qr / sqrt(D),
+      dV = P^T dO.
+    Query rows are grouped by the key set they share, as in the forward."""
+    coords = token_coords(g)
+    kind, _, _, wy, wx = coords
+    T, N = g.n_text, g.n_hr
+    D = qr.shape[1]
+    dq = np.zeros_like(qr, dtype=np.float64)
+    dk = np.zeros_like(kr, dtype=np.float64)
+    dv = np.zeros_like(v, dtype=np.float64)
+    groups = []
+    if T:
+        groups.append(np.arange(T))
+    if g.n_lr:
+        groups.append(np.arange(T + N, g.seq_len))
+    gy, gx = g.grid
+    hr_rows = np.arange(T, T + N)
+    for a in range(gy):
+        for b in range(gx):
+            groups.append(hr_rows[(wy[hr_rows] == a) & (wx[hr_rows] == b)])
+    for rows in groups:
+        if rows.size == 0:
+            continue
+        keys = allowed_keys_of(g, coords, int(rows[0]))
+        p = _softmax_rows((qr[rows] @ kr[keys].T) / math.sqrt(D))
+        dp = do[rows] @ v[keys].T
+        delta = (p * dp).sum(axis=1)
+        ds = p * (dp - delta[:, None])
+        dq[rows] = ds @ kr[keys] / math.sqrt(D)
+        dk[keys] += ds.T @ qr[rows] / math.sqrt(D)
+        dv[keys] += p.T @ do[rows]
+    return dq, dk, dv
+
+
+def backward_head(g: Geometry, q, k, v, do, theta):
+    """Full-layer backward of one head in raster order: (dq, dk, dv) with
+    respect to the un-rotated q, k and v."""
+    _, pr, pc, _, _ = token_coords(g)
+    qr, kr = rope_rotate(q, pr, pc, theta), rope_rotate(k, pr, pc, theta)
+    dqr, dkr, dv = attention_backward_grouped(g, qr, kr, v, do)
+    return rope_rotate_transpose(dqr, pr, pc, theta), rope_rotate_transpose(dkr, pr, pc, theta), dv
+
+
+def backward_query_rows(g: Geometry, q, k, v, do, theta, rows):
+    """dq of selected raster rows of one head (each row needs only its own
+    allowed keys)."""
+    coords = token_coords(g)
+    _, pr, pc, _, _ = coords
+    rows = np.asarray(rows, np.int64)
+    kr = rope_rotate(k, pr, pc, theta)
+    qr = np.zeros_like(q, dtype=np.float64)
+    qr[rows] = rope_rotate(q[rows], pr[rows], pc[rows], theta)
+    D = q.shape[1]
+    out = np.empty((rows.size, D))
+    for idx, i in enumerate(rows):
+        keys = allowed_keys_of(g, coords, int(i))
+        p, _, o = _row_stats(qr, kr, v, int(i), keys)
+        dp = v[keys] @ do[i]
+        ds = p * (dp - do[i] @ o)
+        out[idx] = ds @ kr[keys] / math.sqrt(D)
+    return rope_rotate_transpose(out, pr[rows], pc[rows], theta)
+
+
+def backward_key_rows(g: Geometry, q, k, v, do, theta, keys):
+    """(dk, dv) of selected raster key rows of one head.  Every query that
+    sees one of the keys needs its full softmax row (LSE and output)."""
+    coords = token_coords(g)
+    _, pr, pc, _, _ = coords
+    keys = np.asarray(keys, np.int64)
+    qr = rope_rotate(q, pr, pc, theta)
+    kr = rope_rotate(k, pr, pc, theta)
+    D = q.shape[1]
+    cols = [allowed_queries_of(g, coords, int(j)) for j in keys]
+    need = np.unique(np.concatenate(cols))
+    lse, delta = {}, {}
+    for i in need:
+        kk = allowed_keys_of(g, coords, int(i))
+        _, lse[int(i)], o = _row_stats(qr, kr, v, int(i), kk)
+        delta[int(i)] = do[i] @ o
+    dk = np.empty((keys.size, D))
+    dv = np.empty((keys.size, D))
+    for idx, (j, qs) in enumerate(zip(keys, cols)):
+        s = (qr[qs] @ kr[j]) / math.sqrt(D)
+        p = np.exp(s - np.array([lse[int(i)] for i in qs]))
+        dp = do[qs] @ v[j]
+        ds = p * (dp - np.array([delta[int(i)] for i in qs]))
+        dk[idx] = ds @ qr[qs] / math.sqrt(D)
+        dv[idx] = p @ do[qs]
+    return rope_rotate_transpose(dk, pr[keys], pc[keys], theta), dv

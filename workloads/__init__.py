@@ -12,7 +12,8 @@ length and the ragged 250x380 grid are the evaluation shapes chosen for this
 library; the pages do not state them.  The values stand in for real MMDiT
 activations, which need trained weights: Q, K, V are independent N(0, 1) draws.
 
-Recipe: for workload ``cfg_id``, tensor ``t`` (Q=0, K=1, V=2) and head ``h``,
+Recipe: for workload ``cfg_id``, tensor ``t`` (Q=0, K=1, V=2, and for the
+backward the output gradient dO=3) and head ``h``,
 ``numpy.random.default_rng([2026, cfg_id, t, h]).standard_normal((L, D))`` in
 float64, rounded to float32 (round-to-nearest-even), then for bf16 workloads
 rounded again to bfloat16 (round-to-nearest-even on the float32 bits), then
@@ -25,7 +26,7 @@ from dataclasses import dataclass, asdict
 
 import numpy as np
 
-Q, K, V = 0, 1, 2
+Q, K, V, DO = 0, 1, 2, 3
 
 
 @dataclass(frozen=True)
