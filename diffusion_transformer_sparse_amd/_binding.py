@@ -21,7 +21,8 @@ UG_PLAN_HOST_ONLY = 1
 
 EXPORTED = ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr", "ug_permute",
             "ug_unpermute",
-            "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_status_str", "ug_last_error")
+            "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_attn_fwd_lse", "ug_attn_bwd",
+            "ug_rope2d_bwd", "ug_status_str", "ug_last_error")
 
 
 class UgDesc(ctypes.Structure):
@@ -36,7 +37,8 @@ class UgInfo(ctypes.Structure):
                 ("grid_y", c_int32), ("grid_x", c_int32), ("n_windows", c_int32), ("max_neighbours", c_int32),
                 ("n_neighbour_entries", c_int64), ("pairs_per_head", c_int64), ("eff_flops", c_double),
                 ("workspace_bytes", c_int64), ("attn_tasks", c_int64), ("attn_blocks", c_int64),
-                ("attn_key_tiles", c_int64), ("rope_positions", c_int64)]
+                ("attn_key_tiles", c_int64), ("rope_positions", c_int64), ("bwd_workspace_bytes", c_int64),
+                ("bwd_key_tasks", c_int64), ("bwd_blocks", c_int64)]
 
 
 class UgError(RuntimeError):
@@ -67,13 +69,17 @@ def lib():
         L.ug_attn_fwd.argtypes = [c_void_p] * 7
         L.ug_attn_fwd_raster.argtypes = [c_void_p] * 7
         L.ug_permute_rope.argtypes = [c_void_p] * 6
+        L.ug_attn_fwd_lse.argtypes = [c_void_p] * 8
+        L.ug_attn_bwd.argtypes = [c_void_p] * 12
+        L.ug_rope2d_bwd.argtypes = [c_void_p] * 4
         L.ug_status_str.argtypes = [c_int32]
         L.ug_status_str.restype = c_char_p
         L.ug_last_error.argtypes = []
         L.ug_last_error.restype = c_char_p
         for name in ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr", "ug_permute",
                      "ug_unpermute",
-                     "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster"):
+                     "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_attn_fwd_lse",
+                     "ug_attn_bwd", "ug_rope2d_bwd"):
             getattr(L, name).restype = c_int32
         _lib = L
     return _lib
@@ -262,6 +268,101 @@ def ug_attn_fwd_raster(plan: Plan, q, k, v, o_raster=None, workspace=None):
                                                           c_void_p(v.data_ptr()), c_void_p(o_raster.data_ptr()), ws,
                                                           _stream_ptr(q)))
     return o_raster
+
+
+def _lse_shape(plan: Plan):
+    return (plan.desc.batch, plan.desc.heads, plan.info["seq_len"])
+
+
+def ug_attn_fwd_lse(plan: Plan, q, k, v, o=None, lse=None, workspace=None):
+    """ug_attn_fwd that also returns the natural-log LSE of every row,
+    float32 [B, Hh, L] in the permuted row order."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(plan, t, n)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(_lse_shape(plan), dtype=torch.float32, device=q.device)
+    _check_tensor(plan, o, "o")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != _lse_shape(plan):
+        raise ValueError(f"lse: expected a contiguous float32 tensor of shape {_lse_shape(plan)}")
+    ws = c_void_p(workspace.data_ptr()) if workspace is not None else c_void_p()
+    _check("ug_attn_fwd_lse", lib().ug_attn_fwd_lse(plan.handle, c_void_p(q.data_ptr()), c_void_p(k.data_ptr()),
+                                                    c_void_p(v.data_ptr()), c_void_p(o.data_ptr()),
+                                                    c_void_p(lse.data_ptr()), ws, _stream_ptr(q)))
+    return o, lse
+
+
+def bwd_workspace(plan: Plan, device="cuda"):
+    torch = _torch()
+    return torch.empty(plan.info["bwd_workspace_bytes"], dtype=torch.uint8, device=device)
+
+
+def ug_attn_bwd(plan: Plan, q, k, v, o, d_o, lse, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv) of the attention in the permuted layout (dq, dk
+    with respect to the rotated q, k), given dO, O and the forward's LSE."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")):
+        _check_tensor(plan, t, n)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_tensor(plan, t, n)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != _lse_shape(plan):
+        raise ValueError(f"lse: expected a contiguous float32 tensor of shape {_lse_shape(plan)}")
+    if workspace is None:
+        workspace = bwd_workspace(plan, q.device)
+    vp = lambda t: c_void_p(t.data_ptr())
+    _check("ug_attn_bwd", lib().ug_attn_bwd(plan.handle, vp(q), vp(k), vp(v), vp(o), vp(d_o), vp(lse), vp(dq), vp(dk),
+                                            vp(dv), vp(workspace), _stream_ptr(q)))
+    return dq, dk, dv
+
+
+def ug_rope2d_bwd(plan: Plan, dq_perm, dk_perm):
+    """In place: the transpose of ug_rope2d's rotation (gradients with
+    respect to the rotated Q, K become gradients with respect to Q, K)."""
+    _check_tensor(plan, dq_perm, "dq_perm")
+    _check_tensor(plan, dk_perm, "dk_perm")
+    _check("ug_rope2d_bwd", lib().ug_rope2d_bwd(plan.handle, c_void_p(dq_perm.data_ptr()),
+                                                c_void_p(dk_perm.data_ptr()), _stream_ptr(dq_perm)))
+    return dq_perm, dk_perm
+
+
+class TrainLayer:
+    """Forward that keeps what the backward needs, and the backward of the
+    whole layer (raster in, raster out):
+      forward:  permute+RoPE Q, K; permute V; attention with LSE; unpermute O
+      backward: permute dO; attention backward; RoPE transpose on dQ, dK;
+                unpermute dQ, dK, dV."""
+
+    def __init__(self, plan: Plan, device="cuda"):
+        torch = _torch()
+        self.plan = plan
+        mk = lambda: torch.empty(plan.shape, dtype=torch.bfloat16, device=device)
+        self.qp, self.kp, self.vp, self.op, self.dop = mk(), mk(), mk(), mk(), mk()
+        self.dq, self.dk, self.dv = mk(), mk(), mk()
+        self.lse = torch.empty(_lse_shape(plan), dtype=torch.float32, device=device)
+        self.ws = bwd_workspace(plan, device)
+
+    def forward(self, q, k, v, out):
+        p = self.plan
+        ug_permute_rope(p, q, k, self.qp, self.kp)
+        ug_permute(p, v, self.vp)
+        ug_attn_fwd_lse(p, self.qp, self.kp, self.vp, self.op, self.lse)
+        ug_unpermute(p, self.op, out)
+        return out
+
+    def backward(self, d_out, dq, dk, dv):
+        p = self.plan
+        ug_permute(p, d_out, self.dop)
+        ug_attn_bwd(p, self.qp, self.kp, self.vp, self.op, self.dop, self.lse, self.dq, self.dk, self.dv, self.ws)
+        ug_rope2d_bwd(p, self.dq, self.dk)
+        ug_unpermute(p, self.dq, dq)
+        ug_unpermute(p, self.dk, dk)
+        ug_unpermute(p, self.dv, dv)
+        return dq, dk, dv
 
 
 class Layer:

@@ -2,8 +2,9 @@
 
     python -m diffusion_transformer_sparse_amd.build
 
-Compiles csrc/plan.cpp (host) and csrc/kernels.hip (gfx950 device code) with
-hipcc and links them into diffusion_transformer_sparse_amd/libultragen.so.
+Compiles csrc/plan.cpp (host) and the gfx950 device code (csrc/kernels.hip:
+layout, RoPE and attention forward; csrc/attn_bwd.hip: attention backward)
+with hipcc and links them into diffusion_transformer_sparse_amd/libultragen.so.
 All device code is built with packed-fp32 instructions disabled.
 """
 from __future__ import annotations
@@ -21,6 +22,7 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + os.path.join(ROOT, "include"), "-I/opt/rocm/include"]
+DEVICE_SOURCES = ("kernels.hip", "attn_bwd.hip")
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
 
@@ -40,12 +42,15 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     plan_o = os.path.join(BUILD_DIR, "plan.o")
-    kern_o = os.path.join(BUILD_DIR, "kernels.o")
     _run([HIPCC, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, "plan.cpp"),
           "-o", plan_o], verbose)
-    _run([HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "kernels.hip"), "-o", kern_o], verbose)
+    objs = [plan_o]
+    for src in DEVICE_SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        _run([HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
     tmp = OUT + ".tmp"
-    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, plan_o, kern_o, "-o", tmp], verbose)
+    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, "-o", tmp], verbose)
     os.replace(tmp, OUT)
     return OUT
 

@@ -1,0 +1,602 @@
+// gfx950 kernels of the attention backward (dQ, dK, dV of the composite-
+// masked attention, given dO and the forward's log-sum-exp) and the C-ABI
+// entry point ug_attn_bwd.
+//
+// Method: UltraGen fine-tunes its LR branch through the joint attention
+// ("UltraGen: Efficient Ultra-High-Resolution Image Generation with
+// Hierarchical Local Attention", papernotes.org notes, 关键设计 3 and the
+// training section), so the loss is differentiated through it.  With
+// S = Q K^T / sqrt(D) over the allowed keys and P = exp(S - lse):
+//   Delta_i = dO_i . O_i,  dP = dO V^T,  dS = P * (dP - Delta),
+//   dQ = dS K / sqrt(D),   dK = dS^T Q / sqrt(D),   dV = P^T dO.
+// Three launches, no atomics, every sum taken in a fixed order, so the
+// result is deterministic:
+//   prep   per row and head, lse in log2 units and Delta (fp32) into the
+//          caller's workspace;
+//   dQ     query-major over the forward's query tiles: the keys stream
+//          through LDS in 64-row tiles, as in the forward;
+//   dK/dV  key-major over the plan's transposed tiles: a workgroup owns up
+//          to 256 keys (8 waves x 32) and streams the queries that see
+//          them (Q, dO and their statistics) through LDS.
+// Operands are bf16, products on v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation; P and dS are rounded to bf16 as MFMA operands.
+#include "common.hpp"
+
+#include <algorithm>
+#include <cmath>
+
+namespace {
+
+using namespace ug::dev;
+using ug::host::aligned16;
+using ug::host::check_plan;
+using ug::host::current_device;
+using ug::host::launch_status;
+using ug::host::overlap_ranges;
+using ug::host::tensor_bytes;
+
+constexpr int kThreads = 512;            // 8 waves
+constexpr int kRows = ug::kAttnKeyTile;  // rows per LDS tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+// One 64-row x D bf16 tile in LDS.  Rows are unpadded; the 16-byte chunks of
+// row r are XOR-swizzled so that both ways the kernels read a tile are free
+// of bank conflicts:
+//  - row reads (ds_read_b128, an MFMA operand with the row as the lane
+//    index): 16 consecutive rows of one logical chunk hit 16 different
+//    physical chunk positions;
+//  - transpose reads (ds_read_b64_tr_b16, an operand with the row as the
+//    packed index): an aligned group of 4 rows x 32 dims hits 4 different
+//    64-byte bank groups.
+// For 16-chunk rows the swizzle swaps the two 2-bit halves of r mod 16; for
+// 8-chunk rows (two rows per bank sweep) it does the same on the row pair
+// index.
+template <int D>
+struct Tile {
+  static constexpr int kChunks = D / 8;
+  static constexpr int RB = D * 2;  // bytes per row
+  static constexpr int kBytes = kRows * RB;
+  static constexpr int kLoads = kBytes / 16 / kThreads;  // 16-byte loads per thread and tile
+  static_assert(kChunks == 8 || kChunks == 16, "head_dim must be 64 or 128");
+  static_assert(kLoads >= 1 && kBytes % (16 * kThreads) == 0, "tile must split evenly over the workgroup");
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (kChunks == 16) {
+      return ((r & 3) << 2) | ((r >> 2) & 3);
+    } else {
+      const int m = r >> 1;
+      return ((m & 1) << 2) | ((m >> 1) & 3);
+    }
+  }
+  // byte offset of logical chunk c of row r
+  __device__ static __forceinline__ int off(int r, int c) { return r * RB + ((c ^ swz(r)) << 4); }
+};
+
+// Direct global->LDS loads (global_load_lds_dwordx4) of the 64 rows ks ..
+// ks+63 of a [rows][row_stride] bf16 array: slot s = i*512 + tid of the tile
+// holds row s / kChunks, physical chunk s % kChunks.  A ragged tile (nv < 64)
+// repeats its last row, so no load leaves the range; the kernels mask those
+// rows.
+template <int D>
+struct Loader {
+  using L = Tile<D>;
+  uint32_t off[L::kLoads];
+  __device__ __forceinline__ static int row_of(int i, int tid) { return (i * kThreads + tid) / L::kChunks; }
+  __device__ __forceinline__ static int lchunk_of(int i, int tid) {
+    const int slot = i * kThreads + tid;
+    return (slot % L::kChunks) ^ L::swz(slot / L::kChunks);
+  }
+  __device__ __forceinline__ void init(int64_t rs, int tid) {
+#pragma unroll
+    for (int i = 0; i < L::kLoads; ++i) off[i] = uint32_t(row_of(i, tid) * rs * 2 + lchunk_of(i, tid) * 16);
+  }
+  __device__ __forceinline__ void issue(const __bf16* src, int64_t rs, int32_t ks, int32_t nv, char* tile, int tid,
+                                        int wave) const {
+    const char* base = reinterpret_cast<const char*>(src + int64_t(ks) * rs);  // wave-uniform
+    if (nv == kRows) {
+#pragma unroll
+      for (int i = 0; i < L::kLoads; ++i)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(base + off[i]),
+                                         (lds_void*)(tile + (i * kThreads + wave * 64) * 16), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < L::kLoads; ++i) {
+        const int r = min(row_of(i, tid), nv - 1);
+        const char* gp = base + int64_t(r) * rs * 2 + lchunk_of(i, tid) * 16;
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(gp),
+                                         (lds_void*)(tile + (i * kThreads + wave * 64) * 16), 16, 0, 0);
+      }
+    }
+  }
+};
+
+// Per-lane LDS offsets of the two operand forms; the swizzle depends on the
+// row modulo 16 only, so 32-row blocks and 16-row chunks are constant
+// offsets on top of these.
+//  row[i]:     row l%32, logical chunk 2i + g (dims 16i + 8g .. +7);
+//  tr[t][hh]:  the transpose read of rows 8hh + 4g + (l&15)/4, dims
+//              32t + 16*((l>>4)&1) + 4*(l&3) .. +3 (see tr_operand).
+template <int D>
+struct LaneOffsets {
+  int row[D / 16];
+  int tr[D / 32][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) row[i] = Tile<D>::off(l32, 2 * i + g);
+    const int vrow = 4 * g + ((lane & 15) >> 2);
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      const int dim = 32 * t + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) tr[t][hh] = Tile<D>::off(vrow + 8 * hh, dim / 8) + (dim % 8) * 2;
+    }
+  }
+};
+
+// c (32 tile rows 32mb .. 32mb+31 x 32 register columns) = sum over the D
+// dims of tile[row][dim] * b[column][dim]; b[i] holds dims 16i + 8g .. +7 of
+// the lane's column.  Output lane l: column l%32, rows 8*(j/4) + 4g + j%4.
+// rows_x_rows is the same with the columns read from a 32-row LDS block.
+template <int D>
+__device__ __forceinline__ f32x16 rows_x_regs(const char* tile, int mb, const bf16x8 (&b)[D / 16],
+                                              const LaneOffsets<D>& lo) {
+  const char* t0 = tile + mb * 32 * Tile<D>::RB;
+  f32x16 c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(t0 + lo.row[0]), b[0],
+                                                     f32x16{}, 0, 0, 0);
+#pragma unroll
+  for (int i = 1; i < D / 16; ++i)
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(t0 + lo.row[i]), b[i], c, 0, 0, 0);
+  return c;
+}
+
+template <int D>
+__device__ __forceinline__ f32x16 rows_x_rows(const char* tile, int mb, const char* cols, const LaneOffsets<D>& lo) {
+  const char* t0 = tile + mb * 32 * Tile<D>::RB;
+  f32x16 c = f32x16{};
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i)
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(t0 + lo.row[i]),
+                                                *reinterpret_cast<const bf16x8*>(cols + lo.row[i]), c, 0, 0, 0);
+  return c;
+}
+
+// Transposed operand: lane l gets dim 32t + l%32 of the 8 tile rows
+// {4g .. 4g+3, 8+4g .. 8+4g+3} of 16-row chunk c, the same rows (in the same
+// order) that a 32x32 MFMA output holds in registers 8*(c&1) .. +7 of block
+// c>>1.  Within each 16-lane group the transpose read gives lane j dim j of
+// the four rows the group addresses.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const char* tile, int t, int c, const LaneOffsets<D>& lo) {
+  const char* t0 = tile + 16 * c * Tile<D>::RB;
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t0 + lo.tr[t][0]));
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t0 + lo.tr[t][1]));
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Writes a wave's 32 x D accumulator block (lane l: row l%32; registers j of
+// 32-dim tile t: dims 32t + 8*(j/4) + 4g + j%4), times `scale`, as bf16 to
+// rows row0 .. row0+31 (those < rend) of `out`, through the wave's own
+// 32-row LDS area so that every row is written with 16-byte stores.  The
+// wave reads back only what it wrote: one wave's LDS operations complete in
+// order, so no barrier is needed.
+template <int D>
+__device__ __forceinline__ void store_block(const f32x16 (&acc)[D / 32], float scale, char* ost, __bf16* out,
+                                            int64_t rs, int32_t row0, int32_t rend, int lane) {
+  using L = Tile<D>;
+  const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * t + 8 * q4 + 4 * g;
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = __bf16(acc[t][4 * q4 + e] * scale);
+      *reinterpret_cast<bf16x4*>(ost + L::off(l32, d0 / 8) + (d0 % 8) * 2) = w;
+    }
+  constexpr int rows_per_pass = 64 / L::kChunks;
+#pragma unroll
+  for (int pass = 0; pass < 32 / rows_per_pass; ++pass) {
+    const int r = pass * rows_per_pass + lane / L::kChunks;
+    const int cc = lane % L::kChunks;
+    const uint4 val = *reinterpret_cast<const uint4*>(ost + L::off(r, cc));
+    if (row0 + r < rend) *reinterpret_cast<uint4*>(out + int64_t(row0 + r) * rs + cc * 8) = val;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prep: lse2[bh][row] = lse * log2(e) and delta[bh][row] = sum_d dO * O, in
+// fp32, for rows < L; rows L .. stat_rows-1 are written as zeros.  Each thread
+// owns one 16-byte column chunk of kPrepRows rows; the D/8 chunks of one head
+// are consecutive lanes of a wave and are summed with shuffles.
+// ---------------------------------------------------------------------------
+constexpr int kPrepRows = 4;
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ d_o,
+                                                       const float* __restrict__ lse, float* __restrict__ lse2,
+                                                       float* __restrict__ delta, int32_t L, int32_t Lp,
+                                                       int32_t heads) {
+  constexpr int C = D / 8;  // chunks per head
+  const int32_t units = heads * C;
+  const int32_t b = blockIdx.y;
+  const int64_t boff = int64_t(b) * L * heads * D;
+  for (int r = 0; r < kPrepRows; ++r) {
+    const int32_t row = blockIdx.x * kPrepRows + r;
+    if (row >= Lp) break;
+    for (int32_t c0 = 0; c0 < units; c0 += 256) {  // uniform trip count: every lane shuffles
+      const int32_t c = c0 + int32_t(threadIdx.x);
+      float sum = 0.f;
+      if (c < units && row < L) {
+        const int64_t e = boff + int64_t(row) * heads * D + int64_t(c) * 8;
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + e);
+        const bf16x8 y = *reinterpret_cast<const bf16x8*>(d_o + e);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sum = fmaf(float(x[k]), float(y[k]), sum);
+      }
+#pragma unroll
+      for (int m = C / 2; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, C);
+      if (c < units && c % C == 0) {
+        const int32_t h = c / C;
+        const int64_t s = (int64_t(b) * heads + h) * Lp + row;
+        const bool in = row < L;
+        delta[s] = in ? sum : 0.f;
+        lse2[s] = in ? lse[(int64_t(b) * heads + h) * L + row] * kLog2e : 0.f;
+      }
+    }
+  }
+}
+
+struct BwdParams {
+  const __bf16* q;    // permuted, rotated
+  const __bf16* k;    // permuted, rotated
+  const __bf16* v;
+  const __bf16* d_o;
+  __bf16* dq;
+  __bf16* dk;
+  __bf16* dv;
+  const float* lse2;   // [batch*heads][Lp], log2 units
+  const float* delta;  // [batch*heads][Lp]
+  int64_t row_stride;    // elements between rows (heads * D)
+  int64_t batch_stride;  // elements between batches (L * heads * D)
+  int32_t heads;
+  int32_t Lp;
+  const ug::Task* tasks;
+  const ug::Range* ranges;
+  const ug::Block* blocks;
+  float scale_log2;  // log2(e) / sqrt(D)
+  float scale;       // 1 / sqrt(D)
+};
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per query tile (the forward's tasks), 8 waves x 32
+// queries.  Per wave and 64-key tile (K, V in two-slot LDS rings):
+//   S^T  = K Q^T     (A: K rows from LDS, B: the wave's Q in registers)
+//   dP^T = V dO^T    (A: V rows from LDS, B: the wave's dO in registers)
+//   dS^T = exp2(S^T * scale_log2 - lse2) * (dP^T - Delta)   lane = query
+//   dQ^T += K^T dS^T (A: K transposed from LDS, B: dS^T from registers)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdParams p) {
+  using L = Tile<D>;
+  constexpr int TB = L::kBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];  // K ring [0, 2TB), V ring [2TB, 4TB)
+  __shared__ ug::Range s_rng[ug::kAttnMaxRanges];
+
+  const ug::Block blk = p.blocks[blockIdx.x];
+  if (blk.task < 0) return;  // idle workgroup (uniform)
+  const ug::Task task = p.tasks[blk.task];
+  const int32_t b = blk.bh / p.heads, h = blk.bh - b * p.heads;
+  const int64_t hoff = int64_t(b) * p.batch_stride + int64_t(h) * D;
+  const int64_t rs = p.row_stride;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int32_t qrow = task.q0 + wave * 32 + l32;
+  const int32_t qload = min(qrow, task.q1 - 1);
+
+  const int32_t nr = task.r1 - task.r0;
+  if (tid < nr) s_rng[tid] = p.ranges[task.r0 + tid];
+
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    qf[i] = *reinterpret_cast<const bf16x8*>(p.q + hoff + qload * rs + 16 * i + 8 * g);
+    df[i] = *reinterpret_cast<const bf16x8*>(p.d_o + hoff + qload * rs + 16 * i + 8 * g);
+  }
+  const int64_t srow = int64_t(blk.bh) * p.Lp + qload;
+  const float lse2 = p.lse2[srow];
+  const float dlt = p.delta[srow];
+  const float c2 = p.scale_log2;
+  __syncthreads();  // s_rng is filled
+
+  int32_t ntiles = 0;
+  for (int32_t r = 0; r < nr; ++r) ntiles += (s_rng[r].k1 - s_rng[r].k0 + kRows - 1) / kRows;
+
+  const __bf16* kg = p.k + hoff;
+  const __bf16* vg = p.v + hoff;
+  Loader<D> ld;
+  ld.init(rs, tid);
+  LaneOffsets<D> lo;
+  lo.init(lane);
+  TileCursor cur;
+  cur.init(s_rng, 0, nr);
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+
+  int32_t nv = cur.nv();
+  ld.issue(kg, rs, cur.ks, nv, smem, tid, wave);
+  ld.issue(vg, rs, cur.ks, nv, smem + 2 * TB, tid, wave);
+  cur.advance(s_rng);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int32_t i = 0; i < ntiles; ++i) {
+    const int slot = i & 1;
+    const int32_t nv_next = cur.nv();
+    if (i + 1 < ntiles) {
+      ld.issue(kg, rs, cur.ks, nv_next, smem + (slot ^ 1) * TB, tid, wave);
+      ld.issue(vg, rs, cur.ks, nv_next, smem + 2 * TB + (slot ^ 1) * TB, tid, wave);
+      cur.advance(s_rng);
+    }
+    const char* kt = smem + slot * TB;
+    const char* vt = smem + 2 * TB + slot * TB;
+    bf16x8 dsb[4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x16 s = rows_x_regs<D>(kt, mb, qf, lo);
+      const f32x16 dp = rows_x_regs<D>(vt, mb, df, lo);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = 32 * mb + 8 * (j >> 2) + 4 * g + (j & 3);
+        float pv = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -lse2));
+        if (nv < kRows && key >= nv) pv = 0.f;
+        dsb[2 * mb + (j >> 3)][j & 7] = __bf16(pv * (dp[j] - dlt));
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kt, t, c, lo), dsb[c], acc[t], 0, 0, 0);
+    nv = nv_next;
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of the next tile have landed
+    __syncthreads();
+  }
+  store_block<D>(acc, p.scale, smem + wave * 32 * L::RB, p.dq + hoff, rs, task.q0 + wave * 32, task.q1, lane);
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV: one workgroup per key tile (the plan's transposed tasks), 8 waves x
+// 32 keys.  Per wave and 64-query tile (Q, dO and the rows' lse2 / Delta in
+// two-slot LDS rings), one 32-query block mb at a time:
+//   S  = Q K^T    (A: Q rows from LDS, B: the wave's K in registers)
+//   dP = dO V^T   (A: dO rows from LDS, B: the wave's V rows, kept in LDS:
+//                  K, V and the two accumulators would not fit in registers)
+//   P  = exp2(S * scale_log2 - lse2), dS = P * (dP - Delta)   lane = key
+//   dV^T += dO^T P, dK^T += Q^T dS   (A: dO / Q transposed from LDS)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
+  using L = Tile<D>;
+  constexpr int TB = L::kBytes;
+  constexpr int SB = 2 * kRows * int(sizeof(float));  // lse2 then Delta of 64 rows
+  constexpr int VB = 32 * L::RB;                       // one wave's 32 V rows
+  // Q ring [0, 2TB), dO ring [2TB, 4TB), statistics ring [4TB, 4TB + 2SB),
+  // then the waves' V blocks
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TB + 2 * SB + 8 * VB];
+  __shared__ ug::Range s_rng[ug::kAttnMaxRanges];
+
+  const ug::Block blk = p.blocks[blockIdx.x];
+  if (blk.task < 0) return;  // idle workgroup (uniform)
+  const ug::Task task = p.tasks[blk.task];
+  const int32_t b = blk.bh / p.heads, h = blk.bh - b * p.heads;
+  const int64_t hoff = int64_t(b) * p.batch_stride + int64_t(h) * D;
+  const int64_t rs = p.row_stride;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int32_t krow = task.q0 + wave * 32 + l32;
+  const int32_t kload = min(krow, task.q1 - 1);
+
+  const int32_t nr = task.r1 - task.r0;
+  if (tid < nr) s_rng[tid] = p.ranges[task.r0 + tid];
+
+  bf16x8 kf[D / 16];
+  char* const vblk = smem + 4 * TB + 2 * SB + wave * VB;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    kf[i] = *reinterpret_cast<const bf16x8*>(p.k + hoff + kload * rs + 16 * i + 8 * g);
+    *reinterpret_cast<bf16x8*>(vblk + L::off(l32, 2 * i + g)) =
+        *reinterpret_cast<const bf16x8*>(p.v + hoff + kload * rs + 16 * i + 8 * g);
+  }
+  const float c2 = p.scale_log2;
+  __syncthreads();  // s_rng is filled
+
+  int32_t ntiles = 0;
+  for (int32_t r = 0; r < nr; ++r) ntiles += (s_rng[r].k1 - s_rng[r].k0 + kRows - 1) / kRows;
+
+  const __bf16* qg = p.q + hoff;
+  const __bf16* dog = p.d_o + hoff;
+  const int64_t sbase = int64_t(blk.bh) * p.Lp;
+  Loader<D> ld;
+  ld.init(rs, tid);
+  LaneOffsets<D> lo;
+  lo.init(lane);
+  TileCursor cur;
+  cur.init(s_rng, 0, nr);
+  // rows ks .. ks+63 of the statistics (the workspace is padded past L, so a
+  // whole tile can always be read): wave 0 loads lse2, wave 1 Delta
+  auto issue_stats = [&](int32_t ks, char* dst) {
+    if (wave < 2) {
+      const float* src = (wave == 0 ? p.lse2 : p.delta) + sbase + ks + lane;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void*)(dst + wave * kRows * 4), 4, 0, 0);
+    }
+  };
+
+  f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) dka[t] = dva[t] = f32x16{};
+
+  int32_t nv = cur.nv();
+  ld.issue(qg, rs, cur.ks, nv, smem, tid, wave);
+  ld.issue(dog, rs, cur.ks, nv, smem + 2 * TB, tid, wave);
+  issue_stats(cur.ks, smem + 4 * TB);
+  cur.advance(s_rng);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int32_t i = 0; i < ntiles; ++i) {
+    const int slot = i & 1;
+    const int32_t nv_next = cur.nv();
+    if (i + 1 < ntiles) {
+      ld.issue(qg, rs, cur.ks, nv_next, smem + (slot ^ 1) * TB, tid, wave);
+      ld.issue(dog, rs, cur.ks, nv_next, smem + 2 * TB + (slot ^ 1) * TB, tid, wave);
+      issue_stats(cur.ks, smem + 4 * TB + (slot ^ 1) * SB);
+      cur.advance(s_rng);
+    }
+    const char* qt = smem + slot * TB;
+    const char* dot = smem + 2 * TB + slot * TB;
+    const float* st = reinterpret_cast<const float*>(smem + 4 * TB + slot * SB);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const f32x16 s = rows_x_regs<D>(qt, mb, kf, lo);
+      const f32x16 dp = rows_x_rows<D>(dot, mb, vblk, lo);
+      // one 16-query chunk (registers 8cc .. 8cc+7) at a time: P and dS of
+      // the chunk, then its eight MFMAs
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        bf16x8 pb, dsb;
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2) {
+          const int a = 2 * cc + a2;
+          const int row0 = 32 * mb + 8 * a + 4 * g;  // query rows of registers 4a .. 4a+3
+          const float4 l4 = *reinterpret_cast<const float4*>(st + row0);
+          const float4 d4 = *reinterpret_cast<const float4*>(st + kRows + row0);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 4 * a + e;
+            float pv = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -lv[e]));
+            if (nv < kRows && row0 + e >= nv) pv = 0.f;
+            pb[4 * a2 + e] = __bf16(pv);
+            dsb[4 * a2 + e] = __bf16(pv * (dp[j] - dl[e]));
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+          dva[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(dot, t, 2 * mb + cc, lo), pb, dva[t], 0, 0, 0);
+          dka[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qt, t, 2 * mb + cc, lo), dsb, dka[t], 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 2 * (D / 32); ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        }
+      }
+    }
+    nv = nv_next;
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of the next tile have landed
+    __syncthreads();
+  }
+  char* const ost = smem + wave * 32 * L::RB;
+  store_block<D>(dka, p.scale, ost, p.dk + hoff, rs, task.q0 + wave * 32, task.q1, lane);
+  store_block<D>(dva, 1.0f, ost, p.dv + hoff, rs, task.q0 + wave * 32, task.q1, lane);
+}
+
+template <int D>
+void launch_bwd(ug_plan_t p, BwdParams bp, const __bf16* o, const float* lse, float* lse2, float* delta,
+                hipStream_t s) {
+  const int32_t Lp = int32_t(p->stat_rows());
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(unsigned((Lp + kPrepRows - 1) / kPrepRows), unsigned(p->d.batch)),
+                     dim3(256), 0, s, o, bp.d_o, lse, lse2, delta, int32_t(p->L), Lp, p->d.heads);
+  bp.tasks = p->d_tasks;
+  bp.ranges = p->d_ranges;
+  bp.blocks = p->d_blocks;
+  if (!p->blocks.empty())
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3(unsigned(p->blocks.size())), dim3(kThreads), 0, s, bp);
+  bp.tasks = p->d_ktasks;
+  bp.ranges = p->d_kranges;
+  bp.blocks = p->d_kblocks;
+  if (!p->kblocks.empty())
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3(unsigned(p->kblocks.size())), dim3(kThreads), 0, s, bp);
+}
+
+}  // namespace
+
+extern "C" {
+
+ug_status ug_attn_bwd(ug_plan_t p, const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                      const float* lse, void* dq, void* dk, void* dv, void* workspace, void* stream) {
+  const char* fn = "ug_attn_bwd";
+  ug::clear_error();
+  ug_status st = check_plan(p, fn);
+  if (st != UG_OK) return st;
+  if (p->d.dtype != UG_BF16) return ug::fail(UG_ERR_UNSUPPORTED, "ug_attn_bwd: only bf16 plans are supported");
+  if (p->d.head_dim != 64 && p->d.head_dim != 128)
+    return ug::fail(UG_ERR_UNSUPPORTED, "ug_attn_bwd: head_dim must be 64 or 128");
+  const void* ins[] = {q, k, v, o, d_o};
+  void* outs[] = {dq, dk, dv};
+  for (const void* x : ins)
+    if (!x || !aligned16(x)) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: NULL or unaligned input tensor");
+  for (const void* x : outs)
+    if (!x || !aligned16(x)) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: NULL or unaligned output tensor");
+  if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: NULL or unaligned lse");
+  const int64_t ws_bytes = p->bwd_workspace_bytes();
+  if (!workspace || !aligned16(workspace))
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: workspace must be a 16-byte aligned buffer of "
+                                             "info.bwd_workspace_bytes bytes");
+  const int64_t n = tensor_bytes(p);
+  const int64_t nl = int64_t(p->d.batch) * p->d.heads * p->L * int64_t(sizeof(float));
+  for (int a = 0; a < 3; ++a) {
+    for (int c = a + 1; c < 3; ++c)
+      if (overlap_ranges(outs[a], n, outs[c], n))
+        return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: dq, dk and dv must not overlap");
+    for (const void* x : ins)
+      if (overlap_ranges(outs[a], n, x, n))
+        return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: an output overlaps an input");
+    if (overlap_ranges(outs[a], n, lse, nl) || overlap_ranges(outs[a], n, workspace, ws_bytes))
+      return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: an output overlaps lse or the workspace");
+  }
+  for (const void* x : ins)
+    if (overlap_ranges(workspace, ws_bytes, x, n))
+      return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: the workspace overlaps an input");
+  if (overlap_ranges(workspace, ws_bytes, lse, nl))
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: the workspace overlaps lse");
+  if (p->max_task_ranges > ug::kAttnMaxRanges || p->kmax_task_ranges > ug::kAttnMaxRanges)
+    return ug::fail(UG_ERR_UNSUPPORTED, "ug_attn_bwd: a tile has more row ranges than the kernels stage (" +
+                                            std::to_string(ug::kAttnMaxRanges) + "); use a smaller radius");
+  if (current_device() != p->device)
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: current device is not the plan's device");
+
+  BwdParams bp{};
+  bp.q = static_cast<const __bf16*>(q);
+  bp.k = static_cast<const __bf16*>(k);
+  bp.v = static_cast<const __bf16*>(v);
+  bp.d_o = static_cast<const __bf16*>(d_o);
+  bp.dq = static_cast<__bf16*>(dq);
+  bp.dk = static_cast<__bf16*>(dk);
+  bp.dv = static_cast<__bf16*>(dv);
+  const int64_t stat_elems = int64_t(p->d.batch) * p->d.heads * p->stat_rows();
+  float* lse2 = static_cast<float*>(workspace);
+  float* delta = lse2 + stat_elems;
+  bp.lse2 = lse2;
+  bp.delta = delta;
+  bp.row_stride = int64_t(p->d.heads) * p->d.head_dim;
+  bp.batch_stride = p->L * bp.row_stride;
+  bp.heads = p->d.heads;
+  bp.Lp = int32_t(p->stat_rows());
+  bp.scale = float(1.0 / std::sqrt(double(p->d.head_dim)));
+  bp.scale_log2 = float(1.4426950408889634 / std::sqrt(double(p->d.head_dim)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const __bf16* ob = static_cast<const __bf16*>(o);
+  if (p->d.head_dim == 128)
+    launch_bwd<128>(p, bp, ob, lse, lse2, delta, s);
+  else
+    launch_bwd<64>(p, bp, ob, lse, lse2, delta, s);
+  return launch_status(fn);
+}
+
+}  // extern "C"

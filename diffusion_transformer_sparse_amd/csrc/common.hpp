@@ -1,0 +1,100 @@
+// Definitions shared by the kernel files: vector types, lane-pair
+// reductions, the key-range cursor, and the host-side argument checks of the
+// launchers.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "plan_internal.hpp"
+
+namespace ug {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Lane l and lane l^32 of a wave hold the two halves of one 32x32 MFMA
+// column; these combine them (v_permlane32_swap).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Walks the 64-row tiles of a list of row ranges (key ranges of a query
+// tile, or query ranges of a key tile), one range after another.
+struct TileCursor {
+  int32_t ri, r1, ks, k1;
+  __device__ __forceinline__ void init(const ug::Range* ranges, int32_t r0, int32_t rend) {
+    ri = r0;
+    r1 = rend;
+    const ug::Range r = ranges[r0];
+    ks = r.k0;
+    k1 = r.k1;
+  }
+  __device__ __forceinline__ int32_t nv() const { return min(ug::kAttnKeyTile, k1 - ks); }
+  __device__ __forceinline__ void advance(const ug::Range* ranges) {
+    ks += ug::kAttnKeyTile;
+    if (ks >= k1 && ri + 1 < r1) {
+      ++ri;
+      const ug::Range r = ranges[ri];
+      ks = r.k0;
+      k1 = r.k1;
+    }
+  }
+};
+
+}  // namespace dev
+
+namespace host {
+
+inline ug_status check_plan(ug_plan_t p, const char* fn) {
+  if (!p) return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": plan is NULL");
+  if (p->host_only) return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": plan was built host-only");
+  return UG_OK;
+}
+
+inline bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; }
+
+inline int64_t tensor_bytes(ug_plan_t p) {
+  return int64_t(p->d.batch) * p->L * p->d.heads * p->d.head_dim * (p->d.dtype == UG_BF16 ? 2 : 4);
+}
+
+inline bool overlap(const void* a, const void* b, int64_t n) {
+  const auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + uintptr_t(n) && y < x + uintptr_t(n);
+}
+
+// [a, a + na) and [b, b + nb) share a byte
+inline bool overlap_ranges(const void* a, int64_t na, const void* b, int64_t nb) {
+  const auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + uintptr_t(nb) && y < x + uintptr_t(na);
+}
+
+inline ug_status launch_status(const char* fn) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return ug::fail(UG_ERR_HIP, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
+  return UG_OK;
+}
+
+inline int current_device() {
+  int d = -1;
+  if (hipGetDevice(&d) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  return d;
+}
+
+}  // namespace host
+}  // namespace ug

@@ -18,13 +18,18 @@
 #include <string>
 #include <type_traits>
 
-#include "plan_internal.hpp"
+#include "common.hpp"
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+using namespace ug::dev;
+using ug::host::aligned16;
+using ug::host::check_plan;
+using ug::host::current_device;
+using ug::host::launch_status;
+using ug::host::overlap;
+using ug::host::tensor_bytes;
+
 
 // ---------------------------------------------------------------------------
 // Row gather: dst row j <- src row map(j), whole token rows (all heads) at a
@@ -36,7 +41,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // non-temporal 16-byte vectors; each thread owns one 16-byte column of
 // kGatherRows consecutive rows and has all of them in flight at once.
 // ---------------------------------------------------------------------------
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kGatherRows = 4;  // token rows per workgroup
 
 __global__ __launch_bounds__(1024) void row_gather_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
@@ -77,7 +81,15 @@ __global__ __launch_bounds__(1024) void row_gather_kernel(const u32x4* __restric
 // ---------------------------------------------------------------------------
 constexpr int kRopeRows = 4;  // token rows per workgroup
 
-template <typename T>
+// (cos, sin) of the angle, or of its negation for the transpose (inverse)
+// rotation that carries gradients back through the RoPE.
+template <bool kInverse>
+__device__ __forceinline__ float2 rot(float2 t) {
+  if constexpr (kInverse) t.y = -t.y;
+  return t;
+}
+
+template <typename T, bool kInverse>
 __global__ __launch_bounds__(1024) void rope2d_kernel(T* __restrict__ q, T* __restrict__ k, int32_t L, int32_t T0,
                                                       int32_t N, int32_t W, int32_t lr_w, int32_t rho, int32_t heads,
                                                       int32_t D, const int32_t* __restrict__ perm,
@@ -129,7 +141,7 @@ __global__ __launch_bounds__(1024) void rope2d_kernel(T* __restrict__ q, T* __re
         float* y = reinterpret_cast<float*>(&ka[r]);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const float2 t = tab[p];
+          const float2 t = rot<kInverse>(tab[p]);
           const float a = x[2 * p], b = x[2 * p + 1];
           x[2 * p] = a * t.x - b * t.y;
           x[2 * p + 1] = a * t.y + b * t.x;
@@ -142,7 +154,7 @@ __global__ __launch_bounds__(1024) void rope2d_kernel(T* __restrict__ q, T* __re
         bf16x8 y = *reinterpret_cast<bf16x8*>(&ka[r]);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const float2 t = tab[p];
+          const float2 t = rot<kInverse>(tab[p]);
           const float a = float(x[2 * p]), b = float(x[2 * p + 1]);
           x[2 * p] = __bf16(a * t.x - b * t.y);
           x[2 * p + 1] = __bf16(a * t.y + b * t.x);
@@ -315,10 +327,10 @@ struct AttnParams {
   int32_t T, N;          // text rows, HR rows
   const int32_t* out_perm;     // non-null: write HR output row T+i to raster row T+out_perm[i]
   const int32_t* out_lr_perm;  // non-null (with out_perm): LR row T+N+i to T+N+out_lr_perm[i]
+  float* lse;                  // non-null: natural-log LSE of each row, [batch*heads][lse_rows]
+  int64_t lse_rows;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 template <typename T, int D>
 struct AttnLds {
@@ -343,36 +355,7 @@ struct AttnLds {
   }
 };
 
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
-// Walks the 64-key tiles of a query tile's key ranges.
-struct TileCursor {
-  int32_t ri, r1, ks, k1;
-  __device__ __forceinline__ void init(const ug::Range* ranges, int32_t r0, int32_t rend) {
-    ri = r0;
-    r1 = rend;
-    const ug::Range r = ranges[r0];
-    ks = r.k0;
-    k1 = r.k1;
-  }
-  __device__ __forceinline__ int32_t nv() const { return min(kKT, k1 - ks); }
-  __device__ __forceinline__ void advance(const ug::Range* ranges) {
-    ks += kKT;
-    if (ks >= k1 && ri + 1 < r1) {
-      ++ri;
-      const ug::Range r = ranges[ri];
-      ks = r.k0;
-      k1 = r.k1;
-    }
-  }
-};
 
 // Direct global->LDS loads of one 64-key tile (rows ks .. ks+63).  Slot
 // s = i*512 + tid of the tile holds row s / kChunks, physical chunk
@@ -693,7 +676,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
 
   // ---- epilogue: combine the lane halves' row sums, normalise, and write
   // the wave's 32 x D output block through LDS (swizzled rows) as full rows.
-  const float inv = 1.0f / pair_sum(lsum);
+  const float total = pair_sum(lsum);
+  const float inv = 1.0f / total;
+  if (p.lse && g == 0 && qrow < task.q1)  // log(sum_j exp(s_j)) = (m2 + log2(total)) * ln 2
+    p.lse[int64_t(blk.bh) * p.lse_rows + qrow] = (m2 + __log2f(total)) * 0.6931471805599453f;
   char* const ost = smem + wave * 32 * RB;
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
@@ -745,40 +731,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// launcher helpers
-// ---------------------------------------------------------------------------
-ug_status check_plan(ug_plan_t p, const char* fn) {
-  if (!p) return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": plan is NULL");
-  if (p->host_only) return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": plan was built host-only");
-  return UG_OK;
-}
-
-bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; }
-
-int64_t tensor_bytes(ug_plan_t p) {
-  return int64_t(p->d.batch) * p->L * p->d.heads * p->d.head_dim * (p->d.dtype == UG_BF16 ? 2 : 4);
-}
-
-bool overlap(const void* a, const void* b, int64_t n) {
-  const auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return x < y + uintptr_t(n) && y < x + uintptr_t(n);
-}
-
-ug_status launch_status(const char* fn) {
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return ug::fail(UG_ERR_HIP, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
-  return UG_OK;
-}
-
-int current_device() {
-  int d = -1;
-  if (hipGetDevice(&d) != hipSuccess) {
-    (void)hipGetLastError();
-    return -1;
-  }
-  return d;
-}
 
 ug_status gather(ug_plan_t p, const void* src, void* dst, const int32_t* table, const int32_t* lr_table,
                  hipStream_t s, const char* fn) {
@@ -805,8 +757,8 @@ void launch_attn(ug_plan_t p, const AttnParams& ap, hipStream_t s) {
   hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3(unsigned(p->blocks.size())), dim3(kAttnThreads), 0, s, ap);
 }
 
-ug_status attn_common(ug_plan_t p, const void* q, const void* k, const void* v, void* o, void* workspace,
-                      void* stream, bool raster_out, const char* fn) {
+ug_status attn_common(ug_plan_t p, const void* q, const void* k, const void* v, void* o, float* lse,
+                      void* workspace, void* stream, bool raster_out, const char* fn) {
   ug::clear_error();
   (void)workspace;
   ug_status st = check_plan(p, fn);
@@ -817,6 +769,14 @@ ug_status attn_common(ug_plan_t p, const void* q, const void* k, const void* v, 
   const int64_t n = tensor_bytes(p);
   if (overlap(o, q, n) || overlap(o, k, n) || overlap(o, v, n))
     return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": o overlaps q, k or v");
+  if (lse) {
+    const int64_t nl = int64_t(p->d.batch) * p->d.heads * p->L * int64_t(sizeof(float));
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+      return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": lse must be 4-byte aligned");
+    if (ug::host::overlap_ranges(lse, nl, o, n) || ug::host::overlap_ranges(lse, nl, q, n) ||
+        ug::host::overlap_ranges(lse, nl, k, n) || ug::host::overlap_ranges(lse, nl, v, n))
+      return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": lse overlaps a tensor");
+  }
   if (current_device() != p->device)
     return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": current device is not the plan's device");
   if (p->max_task_ranges > ug::kAttnMaxRanges)
@@ -840,6 +800,8 @@ ug_status attn_common(ug_plan_t p, const void* q, const void* k, const void* v, 
   ap.N = int32_t(p->N);
   ap.out_perm = raster_out ? p->d_perm : nullptr;
   ap.out_lr_perm = raster_out ? p->d_lr_perm : nullptr;
+  ap.lse = lse;
+  ap.lse_rows = p->L;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = p->d.dtype == UG_BF16;
   if (bf && p->d.head_dim == 128)
@@ -850,6 +812,38 @@ ug_status attn_common(ug_plan_t p, const void* q, const void* k, const void* v, 
     launch_attn<float, 128>(p, ap, s);
   else
     launch_attn<float, 64>(p, ap, s);
+  return launch_status(fn);
+}
+
+template <bool kInverse>
+ug_status rope_common(ug_plan_t p, void* q_perm, void* k_perm, void* stream, const char* fn) {
+  ug::clear_error();
+  ug_status st = check_plan(p, fn);
+  if (st != UG_OK) return st;
+  if (!q_perm || !k_perm) return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": NULL tensor");
+  if (!aligned16(q_perm) || !aligned16(k_perm))
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": tensors must be 16-byte aligned");
+  if (overlap(q_perm, k_perm, tensor_bytes(p)))
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": q and k overlap");
+  if (current_device() != p->device)
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": current device is not the plan's device");
+  const int64_t rows = p->N + p->Nlr;
+  if (rows == 0) return UG_OK;
+  const int E = p->d.dtype == UG_BF16 ? 8 : 4;
+  const int64_t units = int64_t(p->d.heads) * p->d.head_dim / E;
+  const dim3 grid(unsigned((rows + kRopeRows - 1) / kRopeRows), unsigned(p->d.batch));
+  const unsigned threads = unsigned(std::min<int64_t>(1024, (units + 63) / 64 * 64));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float2* cs = reinterpret_cast<const float2*>(p->d_rope);
+  const int32_t lr_w = std::max(p->d.lr_w, 1);
+  if (p->d.dtype == UG_BF16)
+    hipLaunchKernelGGL((rope2d_kernel<__bf16, kInverse>), grid, dim3(threads), 0, s, static_cast<__bf16*>(q_perm),
+                       static_cast<__bf16*>(k_perm), int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w,
+                       p->d.rho, p->d.heads, p->d.head_dim, p->d_perm, p->d_lr_perm, cs);
+  else
+    hipLaunchKernelGGL((rope2d_kernel<float, kInverse>), grid, dim3(threads), 0, s, static_cast<float*>(q_perm),
+                       static_cast<float*>(k_perm), int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w,
+                       p->d.rho, p->d.heads, p->d.head_dim, p->d_perm, p->d_lr_perm, cs);
   return launch_status(fn);
 }
 
@@ -868,44 +862,30 @@ ug_status ug_unpermute(ug_plan_t p, const void* x_perm, void* x_raster, void* st
 }
 
 ug_status ug_rope2d(ug_plan_t p, void* q_perm, void* k_perm, void* stream) {
-  ug::clear_error();
-  ug_status st = check_plan(p, "ug_rope2d");
-  if (st != UG_OK) return st;
-  if (!q_perm || !k_perm) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_rope2d: NULL tensor");
-  if (!aligned16(q_perm) || !aligned16(k_perm))
-    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_rope2d: tensors must be 16-byte aligned");
-  if (overlap(q_perm, k_perm, tensor_bytes(p)))
-    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_rope2d: q and k overlap");
-  if (current_device() != p->device)
-    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_rope2d: current device is not the plan's device");
-  const int64_t rows = p->N + p->Nlr;
-  if (rows == 0) return UG_OK;
-  const int E = p->d.dtype == UG_BF16 ? 8 : 4;
-  const int64_t units = int64_t(p->d.heads) * p->d.head_dim / E;
-  const dim3 grid(unsigned((rows + kRopeRows - 1) / kRopeRows), unsigned(p->d.batch));
-  const unsigned threads = unsigned(std::min<int64_t>(1024, (units + 63) / 64 * 64));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const float2* cs = reinterpret_cast<const float2*>(p->d_rope);
-  const int32_t lr_w = std::max(p->d.lr_w, 1);
-  if (p->d.dtype == UG_BF16)
-    hipLaunchKernelGGL(rope2d_kernel<__bf16>, grid, dim3(threads), 0, s, static_cast<__bf16*>(q_perm),
-                       static_cast<__bf16*>(k_perm), int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w,
-                       p->d.rho, p->d.heads, p->d.head_dim, p->d_perm, p->d_lr_perm, cs);
-  else
-    hipLaunchKernelGGL(rope2d_kernel<float>, grid, dim3(threads), 0, s, static_cast<float*>(q_perm),
-                       static_cast<float*>(k_perm), int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w,
-                       p->d.rho, p->d.heads, p->d.head_dim, p->d_perm, p->d_lr_perm, cs);
-  return launch_status("ug_rope2d");
+  return rope_common<false>(p, q_perm, k_perm, stream, "ug_rope2d");
+}
+
+ug_status ug_rope2d_bwd(ug_plan_t p, void* dq_perm, void* dk_perm, void* stream) {
+  return rope_common<true>(p, dq_perm, dk_perm, stream, "ug_rope2d_bwd");
 }
 
 ug_status ug_attn_fwd(ug_plan_t p, const void* q, const void* k, const void* v, void* o, void* workspace,
                       void* stream) {
-  return attn_common(p, q, k, v, o, workspace, stream, false, "ug_attn_fwd");
+  return attn_common(p, q, k, v, o, nullptr, workspace, stream, false, "ug_attn_fwd");
 }
 
 ug_status ug_attn_fwd_raster(ug_plan_t p, const void* q, const void* k, const void* v, void* o_raster,
                              void* workspace, void* stream) {
-  return attn_common(p, q, k, v, o_raster, workspace, stream, true, "ug_attn_fwd_raster");
+  return attn_common(p, q, k, v, o_raster, nullptr, workspace, stream, true, "ug_attn_fwd_raster");
+}
+
+ug_status ug_attn_fwd_lse(ug_plan_t p, const void* q, const void* k, const void* v, void* o, float* lse,
+                          void* workspace, void* stream) {
+  if (!lse) {
+    ug::clear_error();
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_fwd_lse: NULL lse");
+  }
+  return attn_common(p, q, k, v, o, lse, workspace, stream, false, "ug_attn_fwd_lse");
 }
 
 ug_status ug_permute_rope(ug_plan_t p, const void* q_raster, const void* k_raster, void* q_perm, void* k_perm,

@@ -20,6 +20,7 @@
 #include <cstring>
 #include <new>
 #include <numeric>
+#include <stdexcept>
 
 #include "plan_internal.hpp"
 
@@ -182,10 +183,36 @@ void push_merged(std::vector<ug::Range>& out, std::vector<ug::Range> rs) {
   }
 }
 
-int64_t tiles_of(const ug_plan_s& p, const ug::Task& t) {
+int64_t tiles_of(const std::vector<ug::Range>& ranges, const ug::Task& t) {
   int64_t n = 0;
-  for (int r = t.r0; r < t.r1; ++r) n += ceil_div(p.ranges[r].k1 - p.ranges[r].k0, ug::kAttnKeyTile);
+  for (int r = t.r0; r < t.r1; ++r) n += ceil_div(ranges[r].k1 - ranges[r].k0, ug::kAttnKeyTile);
   return n;
+}
+
+// Tiles of rows [q0, q1) that share the row ranges `rs`, appended to a task
+// list: one task per kAttnQueryTile rows.
+void add_tasks(std::vector<ug::Task>& tasks, std::vector<ug::Range>& ranges, int32_t q0, int32_t q1,
+               const std::vector<ug::Range>& rs) {
+  if (q1 <= q0) return;
+  const int32_t r0 = int32_t(ranges.size());
+  push_merged(ranges, rs);
+  const int32_t r1 = int32_t(ranges.size());
+  for (int32_t q = q0; q < q1; q += ug::kAttnQueryTile) tasks.push_back({q, std::min(q1, q + ug::kAttnQueryTile), r0, r1});
+}
+
+// Allowed pairs, 64-row tiles and the most ranges of any task of a list.
+void count_tasks(const std::vector<ug::Task>& tasks, const std::vector<ug::Range>& ranges, int64_t* pairs,
+                 int64_t* tiles, int32_t* max_ranges) {
+  *pairs = 0;
+  *tiles = 0;
+  *max_ranges = 0;
+  for (const auto& t : tasks) {
+    *max_ranges = std::max(*max_ranges, t.r1 - t.r0);
+    int64_t n = 0;
+    for (int r = t.r0; r < t.r1; ++r) n += ranges[r].k1 - ranges[r].k0;
+    *pairs += int64_t(t.q1 - t.q0) * n;
+    *tiles += tiles_of(ranges, t);
+  }
 }
 
 // Query tiles and their key ranges (the composite mask of 关键设计 2):
@@ -194,14 +221,10 @@ int64_t tiles_of(const ug_plan_s& p, const ug::Task& t) {
 //  lr_mode 1 the LR anchors of the neighbouring windows).
 void build_tasks(ug_plan_s& p) {
   const int32_t T = int32_t(p.T), N = int32_t(p.N), L = int32_t(p.L);
-  const int QT = ug::kAttnQueryTile;
   p.tasks.clear();
   p.ranges.clear();
   auto add_rows = [&](int32_t q0, int32_t q1, const std::vector<ug::Range>& rs) {
-    const int32_t r0 = int32_t(p.ranges.size());
-    push_merged(p.ranges, rs);
-    const int32_t r1 = int32_t(p.ranges.size());
-    for (int32_t q = q0; q < q1; q += QT) p.tasks.push_back({q, std::min(q1, q + QT), r0, r1});
+    add_tasks(p.tasks, p.ranges, q0, q1, rs);
   };
   if (T > 0) add_rows(0, T, {{0, T + N}});
   if (p.Nlr > 0) add_rows(T + N, L, {{0, T}, {T + N, L}});
@@ -220,16 +243,45 @@ void build_tasks(ug_plan_s& p) {
       }
     add_rows(T + p.win_off[w], T + p.win_off[w + 1], rs);
   }
-  p.pairs = 0;
-  p.key_tiles = 0;
-  p.max_task_ranges = 0;
-  for (const auto& t : p.tasks) {
-    p.max_task_ranges = std::max(p.max_task_ranges, t.r1 - t.r0);
-    int64_t keys = 0;
-    for (int r = t.r0; r < t.r1; ++r) keys += p.ranges[r].k1 - p.ranges[r].k0;
-    p.pairs += int64_t(t.q1 - t.q0) * keys;
-    p.key_tiles += tiles_of(p, t);
+  count_tasks(p.tasks, p.ranges, &p.pairs, &p.key_tiles, &p.max_task_ranges);
+}
+
+// The same mask seen from the keys, for the dK/dV pass of the backward: key
+// tiles (<= 256 rows of one key group) with the ranges of the queries that
+// attend to them.  Text keys are seen by every query; keys of HR window v by
+// the text queries and the HR queries of the windows around v (the
+// neighbourhood relation is symmetric); LR keys by the HR queries (all of
+// them, or with lr_mode 1 those of the windows around the anchor's window)
+// and by every LR query.  The transposed pair count must equal the forward's.
+void build_key_tasks(ug_plan_s& p) {
+  const int32_t T = int32_t(p.T), N = int32_t(p.N), L = int32_t(p.L);
+  p.ktasks.clear();
+  p.kranges.clear();
+  auto hr_runs_around = [&](int w, std::vector<ug::Range>& rs) {
+    for (int e = p.nbr_off[w]; e < p.nbr_off[w + 1]; ++e) {
+      const int v = p.nbr[e];
+      rs.push_back({T + p.win_off[v], T + p.win_off[v + 1]});
+    }
+  };
+  add_tasks(p.ktasks, p.kranges, 0, T, {{0, L}});
+  for (int w = 0; w < p.nwin; ++w) {
+    std::vector<ug::Range> rs;
+    if (T > 0) rs.push_back({0, T});
+    hr_runs_around(w, rs);
+    add_tasks(p.ktasks, p.kranges, T + p.win_off[w], T + p.win_off[w + 1], rs);
   }
+  if (p.Nlr > 0 && p.d.lr_mode == 0) add_tasks(p.ktasks, p.kranges, T + N, L, {{T, L}});
+  if (p.Nlr > 0 && p.d.lr_mode == 1) {
+    for (int w = 0; w < p.nwin; ++w) {
+      std::vector<ug::Range> rs{{T + N, L}};
+      hr_runs_around(w, rs);
+      add_tasks(p.ktasks, p.kranges, T + N + p.lr_win_off[w], T + N + p.lr_win_off[w + 1], rs);
+    }
+    add_tasks(p.ktasks, p.kranges, T + N + p.lr_win_off[p.nwin], L, {{T + N, L}});
+  }
+  int64_t pairs = 0, tiles = 0;
+  count_tasks(p.ktasks, p.kranges, &pairs, &tiles, &p.kmax_task_ranges);
+  if (pairs != p.pairs) throw std::logic_error("transposed mask pair count differs from the forward's");
 }
 
 // Workgroup order.  Hardware hands workgroup i to XCD i % 8, and each XCD has
@@ -240,15 +292,15 @@ void build_tasks(ug_plan_s& p) {
 // that share neighbour windows and the LR keys run on the same L2.  Queues
 // are balanced by key-tile count and interleaved; short queues are padded
 // with idle workgroups.
-void build_blocks(ug_plan_s& p) {
-  const int64_t BH = int64_t(p.d.batch) * p.d.heads;
+std::vector<ug::Block> order_blocks(const std::vector<ug::Task>& tasks, const std::vector<ug::Range>& ranges,
+                                    int64_t BH) {
   const int X = ug::kXcds;
-  std::vector<int64_t> cost(p.tasks.size());
+  std::vector<int64_t> cost(tasks.size());
   double mean = 0;
-  for (size_t t = 0; t < p.tasks.size(); ++t) mean += double(cost[t] = tiles_of(p, p.tasks[t]));
-  mean /= double(std::max<size_t>(1, p.tasks.size()));
+  for (size_t t = 0; t < tasks.size(); ++t) mean += double(cost[t] = tiles_of(ranges, tasks[t]));
+  mean /= double(std::max<size_t>(1, tasks.size()));
   std::vector<int32_t> long_tasks, normal_tasks;
-  for (size_t t = 0; t < p.tasks.size(); ++t)
+  for (size_t t = 0; t < tasks.size(); ++t)
     (double(cost[t]) > 2.0 * mean ? long_tasks : normal_tasks).push_back(int32_t(t));
 
   std::vector<std::vector<ug::Block>> q(X);
@@ -276,9 +328,16 @@ void build_blocks(ug_plan_s& p) {
     }
   size_t len = 0;
   for (const auto& qq : q) len = std::max(len, qq.size());
-  p.blocks.assign(len * X, ug::Block{-1, 0});
+  std::vector<ug::Block> blocks(len * X, ug::Block{-1, 0});
   for (int xx = 0; xx < X; ++xx)
-    for (size_t k = 0; k < q[xx].size(); ++k) p.blocks[k * X + xx] = q[xx][k];
+    for (size_t k = 0; k < q[xx].size(); ++k) blocks[k * X + xx] = q[xx][k];
+  return blocks;
+}
+
+void build_blocks(ug_plan_s& p) {
+  const int64_t BH = int64_t(p.d.batch) * p.d.heads;
+  p.blocks = order_blocks(p.tasks, p.ranges, BH);
+  p.kblocks = order_blocks(p.ktasks, p.kranges, BH);
 }
 
 template <typename T>
@@ -297,7 +356,8 @@ ug_status upload(const std::vector<T>& h, T** d) {
 }
 
 void free_device(ug_plan_s* p) {
-  void* ptrs[] = {p->d_perm, p->d_inv, p->d_lr_perm, p->d_lr_inv, p->d_rope, p->d_tasks, p->d_ranges, p->d_blocks};
+  void* ptrs[] = {p->d_perm,  p->d_inv,    p->d_lr_perm, p->d_lr_inv,  p->d_rope,
+                  p->d_tasks, p->d_ranges, p->d_blocks,  p->d_ktasks, p->d_kranges, p->d_kblocks};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
   p->d_perm = p->d_inv = nullptr;
@@ -306,6 +366,9 @@ void free_device(ug_plan_s* p) {
   p->d_tasks = nullptr;
   p->d_ranges = nullptr;
   p->d_blocks = nullptr;
+  p->d_ktasks = nullptr;
+  p->d_kranges = nullptr;
+  p->d_kblocks = nullptr;
 }
 
 ug_status check_device(ug_plan_s* p) {
@@ -349,10 +412,14 @@ ug_status ug_plan(const ug_desc* desc, ug_plan_t* out) {
     ug::build_lr_windows(*p);
     ug::build_rope(*p);
     ug::build_tasks(*p);
+    ug::build_key_tasks(*p);
     ug::build_blocks(*p);
   } catch (const std::bad_alloc&) {
     delete p;
     return ug::fail(UG_ERR_OUT_OF_MEMORY, "ug_plan: host allocation failed");
+  } catch (const std::logic_error& e) {
+    delete p;
+    return ug::fail(UG_ERR_INTERNAL, std::string("ug_plan: ") + e.what());
   } catch (...) {
     delete p;
     return ug::fail(UG_ERR_INTERNAL, "ug_plan: unexpected exception");
@@ -367,6 +434,9 @@ ug_status ug_plan(const ug_desc* desc, ug_plan_t* out) {
     if (s == UG_OK) s = ug::upload(p->tasks, &p->d_tasks);
     if (s == UG_OK) s = ug::upload(p->ranges, &p->d_ranges);
     if (s == UG_OK) s = ug::upload(p->blocks, &p->d_blocks);
+    if (s == UG_OK) s = ug::upload(p->ktasks, &p->d_ktasks);
+    if (s == UG_OK) s = ug::upload(p->kranges, &p->d_kranges);
+    if (s == UG_OK) s = ug::upload(p->kblocks, &p->d_kblocks);
     if (s != UG_OK) {
       ug::free_device(p);
       delete p;
@@ -405,6 +475,9 @@ ug_status ug_plan_info(ug_plan_t p, ug_info* out) {
   out->attn_blocks = int64_t(p->blocks.size());
   out->attn_key_tiles = p->key_tiles;
   out->rope_positions = p->rope_P;
+  out->bwd_workspace_bytes = p->bwd_workspace_bytes();
+  out->bwd_key_tasks = int64_t(p->ktasks.size());
+  out->bwd_blocks = int64_t(p->kblocks.size());
   return UG_OK;
 }
 

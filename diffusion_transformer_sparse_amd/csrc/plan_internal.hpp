@@ -11,7 +11,9 @@
 namespace ug {
 
 // One query tile of the attention: query rows [q0, q1) (at most 256 rows,
-// all sharing one key set) and its key ranges ranges[r0 .. r1).
+// all sharing one key set) and its key ranges ranges[r0 .. r1).  The
+// backward's key-major tasks use the same record for a key tile: key rows
+// [q0, q1) and the ranges of the queries that see them.
 struct Task {
   int32_t q0, q1, r0, r1;
 };
@@ -52,6 +54,19 @@ struct ug_plan_s {
   int64_t key_tiles = 0;  // 64-key tiles per (batch, head)
   int32_t max_nbr = 0;
   int32_t max_task_ranges = 0;  // most key ranges of any query tile
+  // key-major view of the mask (backward dK/dV pass): key tiles with the
+  // query ranges that see them, and their workgroup order
+  std::vector<ug::Task> ktasks;
+  std::vector<ug::Range> kranges;
+  std::vector<ug::Block> kblocks;
+  int32_t kmax_task_ranges = 0;
+
+  // Backward statistics (log2-scaled LSE and Delta per row) live in the
+  // caller's workspace as two [batch*heads][stat_rows] float arrays; the rows
+  // past L are padding (zeros), so a 64-row tile starting at any row < L can
+  // be read whole.
+  int64_t stat_rows() const { return (L + 64 + 63) / 64 * 64; }
+  int64_t bwd_workspace_bytes() const { return 2 * int64_t(d.batch) * d.heads * stat_rows() * int64_t(sizeof(float)); }
 
   // device copies (owned)
   int32_t* d_perm = nullptr;
@@ -62,6 +77,9 @@ struct ug_plan_s {
   ug::Task* d_tasks = nullptr;
   ug::Range* d_ranges = nullptr;
   ug::Block* d_blocks = nullptr;
+  ug::Task* d_ktasks = nullptr;
+  ug::Range* d_kranges = nullptr;
+  ug::Block* d_kblocks = nullptr;
 };
 
 namespace ug {

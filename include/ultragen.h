@@ -110,6 +110,9 @@ typedef struct ug_info {
   int64_t attn_blocks;         /* workgroups one ug_attn_fwd launches */
   int64_t attn_key_tiles;      /* 64-key tiles processed per (batch, head) */
   int64_t rope_positions;      /* rows of the RoPE cos/sin table */
+  int64_t bwd_workspace_bytes; /* bytes ug_attn_bwd needs as workspace */
+  int64_t bwd_key_tasks;       /* key tiles per (batch, head) of the dK/dV pass */
+  int64_t bwd_blocks;          /* workgroups one dK/dV pass launches */
 } ug_info;
 
 typedef struct ug_plan_s* ug_plan_t;
@@ -201,6 +204,47 @@ ug_status ug_permute_rope(ug_plan_t plan, const void* q_raster, const void* k_ra
                           void* k_perm, void* stream);
 ug_status ug_attn_fwd_raster(ug_plan_t plan, const void* q, const void* k, const void* v, void* o_raster,
                              void* workspace, void* stream);
+
+/*
+ * Training path.  UltraGen fine-tunes its LR branch through the joint
+ * attention (关键设计 3 and the training section: LoRA on the LR Q, K, V
+ * projections, flow-matching loss), so the layer needs its gradients.
+ * ug_attn_bwd works on bf16 plans with head_dim 64 or 128 (otherwise
+ * UG_ERR_UNSUPPORTED); ug_attn_fwd_lse and ug_rope2d_bwd accept every plan
+ * their forward counterparts accept.
+ *
+ * ug_attn_fwd_lse: ug_attn_fwd that also writes lse[B][Hh][L] (float32,
+ * 4-byte aligned, rows in the permuted order): the natural log of each row's
+ * softmax denominator, log(sum over allowed j of exp(q.k_j / sqrt(D))).
+ * lse must not overlap q, k, v or o.
+ *
+ * ug_attn_bwd: gradients of the same attention, in the permuted layout, given
+ * dO (d_o), the forward's output o and lse:
+ *   dq, dk = dL/dQ, dL/dK with respect to the rotated (ug_rope2d'ed) Q and
+ *   K; dv = dL/dV.  With P = exp(S - lse), S = QK^T/sqrt(D) over the allowed
+ *   keys, Delta_i = dO_i . O_i and dS = P * (dO V^T - Delta):
+ *   dq = dS K / sqrt(D), dk = dS^T Q / sqrt(D), dv = P^T dO.
+ * `workspace` (caller-owned, 16-byte aligned, info.bwd_workspace_bytes) holds
+ * per-row statistics; its contents need no initialisation.  Outputs are
+ * written in full (no accumulation into them) and must not overlap each
+ * other, the inputs, lse or the workspace.  The result does not depend on
+ * scheduling (no atomics).  Products in bf16 MFMA with fp32 accumulation;
+ * P and dS are rounded to bf16 as MFMA operands.
+ *
+ * ug_rope2d_bwd: in place on permuted dq and dk, the transpose of
+ * ug_rope2d's rotation (each pair turns by the negated angle), which maps
+ * gradients with respect to the rotated Q, K to gradients with respect to
+ * Q, K.  Same arguments and rules as ug_rope2d.
+ *
+ * A layer's backward in raster layout is then: ug_permute(dO) ->
+ * ug_attn_bwd -> ug_rope2d_bwd(dq, dk) -> ug_unpermute of dq, dk and dv.
+ */
+ug_status ug_attn_fwd_lse(ug_plan_t plan, const void* q, const void* k, const void* v, void* o, float* lse,
+                          void* workspace, void* stream);
+ug_status ug_attn_bwd(ug_plan_t plan, const void* q, const void* k, const void* v, const void* o,
+                      const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                      void* stream);
+ug_status ug_rope2d_bwd(ug_plan_t plan, void* dq_perm, void* dk_perm, void* stream);
 
 const char* ug_status_str(ug_status s);
 const char* ug_last_error(void);

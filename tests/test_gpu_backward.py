@@ -1,0 +1,274 @@
+"""GPU parity of the training path (forward LSE, attention backward, RoPE
+transpose) against the fp64 oracle on the same seeded inputs.
+
+Bars for bf16 (8 significant bits: unit roundoff u = 2^-8; a round-to-nearest
+step has an RMS relative error of about 0.4u = 1.6e-3), derived from the
+rounding steps of the kernels (operands rounded to bf16, fp32 accumulation):
+  - the rotated Q, K are bf16, so every logit carries an RMS error of about
+    sqrt(2) * 1.6e-3, and P a relative error of about 2.2e-3;
+  - P and dS are rounded to bf16 as MFMA operands, O (used for Delta) carries
+    the forward's error (~3e-3 rel-L2), and the outputs are rounded to bf16;
+  first-order propagation gives rel-L2 of about 3e-3 (dV) to 5e-3 (dK, which
+  also passes the RoPE transpose), hence rel-L2 <= 1e-2 per segment and
+  max-abs <= 2e-2 * max|ref| (about 5u) per segment; LSE |error| <= 4u *
+  q_scale (bf16) or 1e-5 (fp32); a RoPE round trip (two roundings of a
+  rotated pair) is within (sqrt(2) + 1)u <= 3u of the pair's norm.
+"""
+import numpy as np
+import pytest
+
+import workloads as WL
+from oracle import ultragen_oracle as O
+from tests.gpu_util import seg_errors, to_device, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+BWD_REL = 1e-2
+BWD_MAXREL = 2e-2
+U_BF16 = 2.0 ** -8  # unit roundoff of bfloat16
+
+SMALL_BWD = ["small_ragged", "small_d64", "small_ragged_corr"]
+
+
+@pytest.fixture(scope="module")
+def U():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import diffusion_transformer_sparse_amd as U
+    return U
+
+
+def permuted_order(w):
+    T, N = w.n_text, w.n_hr
+    perm = O.window_first_perm(w.hr_h, w.hr_w, w.window)
+    lr = O.lr_window_first_perm(O.geometry_of(w)) if w.lr_mode == 1 else np.arange(w.n_lr)
+    return np.concatenate([np.arange(T), T + perm, T + N + lr]).astype(np.int64)
+
+
+def grad_close(got, ref, w, what, rows=None):
+    errs = seg_errors(got, ref, w, rows)
+    idx = np.arange(got.shape[0]) if rows is None else np.asarray(rows)
+    T, N = w.n_text, w.n_hr
+    kinds = np.where(idx < T, 0, np.where(idx < T + N, 1, 2))
+    bad = {}
+    for k, name in enumerate(("text", "hr", "lr")):
+        if name not in errs:
+            continue
+        scale = float(np.abs(ref[kinds == k]).max())
+        mx, rel = errs[name]
+        if mx > BWD_MAXREL * scale or rel > BWD_REL:
+            bad[name] = (mx, scale, rel)
+    assert not bad, f"{what}: (max-abs, max|ref|, rel-L2) {bad} exceed ({BWD_MAXREL}*max|ref|, {BWD_REL})"
+
+
+def inputs(w):
+    return [to_device(WL.tensor_storage(w, t), w.dtype) for t in (WL.Q, WL.K, WL.V, WL.DO)]
+
+
+def oracle_heads(w, heads, b=0):
+    geo = O.geometry_of(w)
+    for h in heads:
+        yield h, geo, [WL.head_f64(w, t, h, b) for t in (WL.Q, WL.K, WL.V, WL.DO)]
+
+
+# ---------------------------------------------------------------- forward LSE
+
+@pytest.mark.parametrize("name,qscale", [("tiny_masked", 1.0), ("small_ragged", 1.0), ("small_d64", 1.0),
+                                         ("small_ragged_corr", 1.0), ("small_ragged", 8.0),
+                                         ("small_ragged_f32", 1.0)])
+def test_forward_lse_matches_oracle(U, name, qscale):
+    import torch
+    w = WL.WORKLOADS[name].with_(q_scale=qscale)
+    p = U.ug_plan(U.desc_of(w))
+    q, k, v, _ = inputs(w)
+    qp, kp = U.ug_permute_rope(p, q, k)
+    vp = U.ug_permute(p, v)
+    o, lse = U.ug_attn_fwd_lse(p, qp, kp, vp)
+    o_ref = U.ug_attn_fwd(p, qp, kp, vp)
+    torch.cuda.synchronize()
+    bits = torch.int16 if w.dtype == "bf16" else torch.int32
+    assert torch.equal(o.view(bits), o_ref.view(bits)), "the LSE variant changed O"
+    order = permuted_order(w)
+    got = lse.cpu().numpy().astype(np.float64)[0]
+    tol = 4 * U_BF16 * qscale if w.dtype == "bf16" else 1e-5
+    for h, geo, (qh, kh, _, _) in oracle_heads(w, range(w.heads)):
+        _, pr, pc, _, _ = O.token_coords(geo)
+        ref = O.lse_grouped(geo, O.rope_rotate(qh, pr, pc, w.rope_theta), O.rope_rotate(kh, pr, pc, w.rope_theta))
+        err = np.abs(got[h] - ref[order])
+        assert err.max() <= tol, (h, float(err.max()), tol)
+
+
+# ---------------------------------------------------------------- RoPE transpose
+
+@pytest.mark.parametrize("name", ["small_ragged", "small_ragged_f32", "small_ragged_corr"])
+def test_rope2d_bwd_inverts_rope2d(U, name):
+    import torch
+    w = WL.WORKLOADS[name]
+    p = U.ug_plan(U.desc_of(w))
+    q, k, _, _ = inputs(w)
+    qp, kp = U.ug_permute(p, q), U.ug_permute(p, k)
+    q0, k0 = qp.clone(), kp.clone()
+    U.ug_rope2d(p, qp, kp)
+    U.ug_rope2d_bwd(p, qp, kp)
+    torch.cuda.synchronize()
+    for a, b in ((qp, q0), (kp, k0)):
+        a, b = to_host_f64(a, w.dtype), to_host_f64(b, w.dtype)
+        # a rotation mixes the two elements of a pair, so each rounding error
+        # is bounded by u times the pair's norm, not the element's magnitude
+        pair = np.sqrt(b[..., 0::2] ** 2 + b[..., 1::2] ** 2).repeat(2, axis=-1)
+        bound = 3 * U_BF16 * pair + 1e-6 if w.dtype == "bf16" else 4e-7 * pair + 1e-6
+        assert np.all(np.abs(a - b) <= bound), float((np.abs(a - b) / (pair + 1e-30)).max())
+
+
+def test_rope2d_bwd_matches_oracle_transpose(U):
+    import torch
+    w = WL.WORKLOADS["small_ragged_f32"]
+    p = U.ug_plan(U.desc_of(w))
+    q, k, _, _ = inputs(w)
+    qp, kp = U.ug_permute(p, q), U.ug_permute(p, k)
+    U.ug_rope2d_bwd(p, qp, kp)
+    torch.cuda.synchronize()
+    order = permuted_order(w)
+    geo = O.geometry_of(w)
+    _, pr, pc, _, _ = O.token_coords(geo)
+    got = to_host_f64(qp, w.dtype)[0]
+    for h in range(w.heads):
+        ref = O.rope_rotate_transpose(WL.head_f64(w, WL.Q, h), pr, pc, w.rope_theta)[order]
+        assert np.abs(got[:, h] - ref).max() <= 2e-6
+
+
+# ---------------------------------------------------------------- attention backward
+
+def run_attn_bwd(U, w):
+    """permuted layout, no RoPE: forward with LSE, backward; raster results."""
+    import torch
+    p = U.ug_plan(U.desc_of(w))
+    q, k, v, do = inputs(w)
+    qp, kp, vp, dop = (U.ug_permute(p, x) for x in (q, k, v, do))
+    o, lse = U.ug_attn_fwd_lse(p, qp, kp, vp)
+    dq, dk, dv = U.ug_attn_bwd(p, qp, kp, vp, o, dop, lse)
+    out = [to_host_f64(U.ug_unpermute(p, x), w.dtype)[0] for x in (dq, dk, dv)]
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name,qscale", [(n, 1.0) for n in SMALL_BWD] + [("small_ragged", 8.0)])
+def test_attention_backward_matches_oracle(U, name, qscale):
+    w = WL.WORKLOADS[name].with_(q_scale=qscale)
+    dq, dk, dv = run_attn_bwd(U, w)
+    for h, geo, (qh, kh, vh, doh) in oracle_heads(w, range(w.heads)):
+        rq, rk, rv = O.attention_backward_grouped(geo, qh, kh, vh, doh)
+        grad_close(dq[:, h], rq, w, f"{name} x{qscale} dq h{h}")
+        grad_close(dk[:, h], rk, w, f"{name} x{qscale} dk h{h}")
+        grad_close(dv[:, h], rv, w, f"{name} x{qscale} dv h{h}")
+
+
+def run_layer_bwd(U, w):
+    import torch
+    p = U.ug_plan(U.desc_of(w))
+    q, k, v, do = inputs(w)
+    layer = U.TrainLayer(p)
+    out = torch.empty_like(q)
+    layer.forward(q, k, v, out)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    layer.backward(do, dq, dk, dv)
+    torch.cuda.synchronize()
+    return p, [to_host_f64(x, w.dtype) for x in (out, dq, dk, dv)]
+
+
+@pytest.mark.parametrize("name", SMALL_BWD + ["1k"])
+def test_layer_backward_matches_oracle(U, name):
+    """TrainLayer (raster in, raster out: RoPE, permutation, attention and
+    their backward) against the oracle's full-layer backward."""
+    w = WL.WORKLOADS[name]
+    _, (out, dq, dk, dv) = run_layer_bwd(U, w)
+    heads = range(w.heads) if w.heads <= 4 else (0, 11, w.heads - 1)
+    for h, geo, (qh, kh, vh, doh) in oracle_heads(w, heads):
+        rq, rk, rv = O.backward_head(geo, qh, kh, vh, doh, w.rope_theta)
+        grad_close(dq[0][:, h], rq, w, f"{name} dq h{h}")
+        grad_close(dk[0][:, h], rk, w, f"{name} dk h{h}")
+        grad_close(dv[0][:, h], rv, w, f"{name} dv h{h}")
+
+
+EDGE_BWD = {
+    "no_text": dict(n_text=0),
+    "no_lr": dict(lr_h=0, lr_w=0),
+    "one_text": dict(n_text=1),
+    "radius0": dict(radius=0),
+    "radius2": dict(radius=2),
+    "window8": dict(window=8),
+    "window_covers_grid": dict(window=64),
+    "batch2": dict(batch=2),
+    "corr_overhang": dict(lr_mode=1, lr_h=14, lr_w=14),
+}
+
+
+@pytest.mark.parametrize("case", list(EDGE_BWD))
+def test_layer_backward_edge_cases(U, case):
+    w = WL.WORKLOADS["small_ragged"].with_(cfg_id=21, heads=2, **EDGE_BWD[case])
+    _, (_, dq, dk, dv) = run_layer_bwd(U, w)
+    for b in range(w.batch):
+        for h, geo, (qh, kh, vh, doh) in oracle_heads(w, range(w.heads), b):
+            rq, rk, rv = O.backward_head(geo, qh, kh, vh, doh, w.rope_theta)
+            for got, ref, n in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+                grad_close(got[b][:, h], ref, w, f"{case} {n} b{b} h{h}")
+
+
+def test_backward_is_deterministic(U):
+    import torch
+    w = WL.WORKLOADS["1k"]
+    p = U.ug_plan(U.desc_of(w))
+    q, k, v, do = inputs(w)
+    o, lse = U.ug_attn_fwd_lse(p, q, k, v)
+    a = U.ug_attn_bwd(p, q, k, v, o, do, lse)
+    b = U.ug_attn_bwd(p, q, k, v, o, do, lse)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["4k", "4k_corr"])
+def test_full_size_backward_sampled(U, name):
+    """The 256x256 layer's backward at full size; the oracle recomputes dq of
+    sampled query rows (corner, edge, interior HR, text, LR) and dk, dv of
+    sampled HR key rows one by one."""
+    w = WL.WORKLOADS[name]
+    _, (_, dq, dk, dv) = run_layer_bwd(U, w)
+    geo = O.geometry_of(w)
+    T, W = w.n_text, w.hr_w
+    qrows = np.array([0, T - 1, T, T + 15 * W + 16, T + 100 * W + 37, T + w.n_hr - 1, T + w.n_hr,
+                      w.seq_len - 1])
+    krows = np.array([T + 16 * W + 16, T + 255 * W + 3])
+    for h in (0, w.heads - 1):
+        qh, kh, vh, doh = (WL.head_f64(w, t, h) for t in (WL.Q, WL.K, WL.V, WL.DO))
+        rq = O.backward_query_rows(geo, qh, kh, vh, doh, w.rope_theta, qrows)
+        grad_close(dq[0][qrows, h], rq, w, f"{name} dq h{h}", qrows)
+        rk, rv = O.backward_key_rows(geo, qh, kh, vh, doh, w.rope_theta, krows)
+        grad_close(dk[0][krows, h], rk, w, f"{name} dk h{h}", krows)
+        grad_close(dv[0][krows, h], rv, w, f"{name} dv h{h}", krows)
+
+
+def test_backward_argument_errors(U):
+    import ctypes
+    import torch
+    w = WL.WORKLOADS["small_ragged"]
+    p = U.ug_plan(U.desc_of(w))
+    q, k, v, do = inputs(w)
+    o, lse = U.ug_attn_fwd_lse(p, q, k, v)
+    lib = U.lib()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ws = U.bwd_workspace(p)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    assert lib.ug_attn_bwd(p.handle, vp(q), vp(k), vp(v), vp(o), vp(do), vp(lse), vp(dq), vp(dk), vp(dv), None,
+                           s) == 1
+    assert lib.ug_attn_bwd(p.handle, vp(q), vp(k), vp(v), vp(o), vp(do), vp(lse), vp(dq), vp(dq), vp(dv), vp(ws),
+                           s) == 1
+    assert lib.ug_attn_bwd(p.handle, vp(q), vp(k), vp(v), vp(o), vp(do), vp(lse), vp(q), vp(dk), vp(dv), vp(ws),
+                           s) == 1
+    assert lib.ug_attn_fwd_lse(p.handle, vp(q), vp(k), vp(v), vp(o), None, None, s) == 1
+    wf = WL.WORKLOADS["small_ragged_f32"]
+    pf = U.ug_plan(U.desc_of(wf))
+    assert lib.ug_attn_bwd(pf.handle, vp(q), vp(k), vp(v), vp(o), vp(do), vp(lse), vp(dq), vp(dk), vp(dv), vp(ws),
+                           s) == 2
+    torch.cuda.synchronize()
