@@ -14,6 +14,12 @@ Prints ONE JSON line.  `value` is effective TFLOP/s of the whole step:
 4 * D * (allowed query-key pairs) * heads / step time, i.e. only unmasked
 pairs count.  Per-kernel times come from HIP events recorded on the stream
 the kernels are launched on (torch's current stream).
+
+For bf16 workloads the line also carries "backward": the training layer's
+backward step (permute dO, attention backward, RoPE transpose, unpermute dQ,
+dK, dV) after a forward that saved the LSE, with the attention backward's
+effective TFLOP/s counted as 10 * D * pairs * heads (the five products S,
+dP, dV, dK, dQ of the allowed pairs).
 """
 from __future__ import annotations
 
@@ -87,6 +93,7 @@ def main():
     ap.add_argument("--workload", default="4k")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward step measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -171,6 +178,42 @@ def main():
     ums_step, uavg = timed(step_unfused, 5, max(5, args.steps // 2), 2)
     ums_perm3, ums_rope, ums_attn, ums_unperm = uavg(0, 1), uavg(1, 2), uavg(2, 3), uavg(3, 4)
 
+    backward = None
+    if w.dtype == "bf16" and not args.no_backward:
+        d_o = to_dev(WL.tensor_storage(w, WL.DO))
+        train = U.TrainLayer(plan, dev)
+        grads = [torch.empty_like(q) for _ in range(3)]
+        train.forward(q, k, v, out)
+
+        def step_bwd(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            U.ug_permute(plan, d_o, train.dop)
+            if ev is not None:
+                ev[1].record(stream)
+            U.ug_attn_bwd(plan, train.qp, train.kp, train.vp, train.op, train.dop, train.lse, train.dq, train.dk,
+                          train.dv, train.ws)
+            if ev is not None:
+                ev[2].record(stream)
+            U.ug_rope2d_bwd(plan, train.dq, train.dk)
+            for src, dst in zip((train.dq, train.dk, train.dv), grads):
+                U.ug_unpermute(plan, src, dst)
+            if ev is not None:
+                ev[3].record(stream)
+
+        bms_step, bavg = timed(step_bwd, 4, max(5, args.steps // 5), 2)
+        bms_attn = bavg(1, 2)
+        bflops = 2.5 * info["eff_flops"]
+        backward = {
+            "ms_per_step": round(bms_step, 4),
+            "step": "ug_permute(dO) + ug_attn_bwd + ug_rope2d_bwd(dQ,dK) + ug_unpermute(dQ,dK,dV)",
+            "attn_bwd": {"ms": round(bms_attn, 4), "eff_tflops": round(bflops / (bms_attn * 1e-3) / 1e12, 2),
+                         "frac_peak": round(bflops / (bms_attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "eff_flop": bflops},
+            "layout_ms": round(bavg(0, 1) + bavg(2, 3), 4),
+        }
+        del train, grads, d_o
+
     esize = 2 if w.dtype == "bf16" else 4
     tbytes = w.batch * w.seq_len * w.heads * w.head_dim * esize
     rope_bytes = 2 * 2 * w.batch * (w.n_hr + w.n_lr) * w.heads * w.head_dim * esize
@@ -220,6 +263,7 @@ def main():
             "rope2d_qk": hbm(rope_bytes, ums_rope),
             "unpermute_o": hbm(2 * tbytes, ums_unperm),
         },
+        "backward": backward,
         "plan_build_s": round(t_plan, 4),
         "kernel_sha": kernel_hash(),
     }
