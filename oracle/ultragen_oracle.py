@@ -23,6 +23,11 @@ Sources (cited by page title and section):
         section: the LR branch is fine-tuned (LoRA on its Q, K, V
         projections) by gradient descent on the flow-matching loss, so the
         loss is differentiated through the joint attention.
+  [KD4] same page, 关键设计 4 (guidance-weighted warm start): the LR latent is
+        upsampled by interpolation and sharpened into a reference, and the HR
+        start latent is alpha * X_T + (1 - alpha) * reference, alpha = t/T;
+        [GS] section 2.C repeats it (upsampled, sharpened, added at an
+        intermediate timestep).
 
 Everything is computed in float64, in RASTER order (text rows, then HR rows
 r*W + c, then LR rows m*w + n), and every mask decision is taken from 2D
@@ -54,6 +59,15 @@ open (all listed in the design doc's table of readings):
      mask, softmax, PV) with respect to the raster Q, K, V, given dO; the
      log-sum-exp saved by the forward is the natural log of the softmax
      denominator of the scaled logits q.k/sqrt(D).
+  R12 warm start [KD4]: the pages name the steps but not the operators.
+     Interpolation is bilinear on the HR grid with LR sample (m, n) at HR
+     position (rho*m, rho*n) (the coordinate map of [KD2]); HR rows/columns
+     past the last sample take its value.  Sharpening is unsharp masking,
+     Y = U + s * (U - B*U), B the 3x3 binomial blur ([1 2 1]/4 both ways) with
+     edges replicated, strength s a parameter (0 = none).  The noising at
+     time t is the blend itself: alpha * X_T + (1 - alpha) * Y with alpha =
+     t/T is the rectified-flow noising of Y at t, and the formula for the
+     reference carries no noise term of its own.  X_T (Gaussian) is an input.
 """
 from __future__ import annotations
 
@@ -527,3 +541,50 @@ def backward_key_rows(g: Geometry, q, k, v, do, theta, keys):
         dk[idx] = ds @ qr[qs] / math.sqrt(D)
         dv[idx] = p @ do[qs]
     return rope_rotate_transpose(dk, pr[keys], pc[keys], theta), dv
+
+
+# --------------------------------------------------------------------------
+# Warm start ([KD4], R12): X_hr = alpha * noise + (1 - alpha) * sharpen(up(X_lr))
+# on latents laid out [H, W, C] (HR) and [h, w, C] (LR), channels last.
+# --------------------------------------------------------------------------
+
+def upsample_bilinear(x_lr: np.ndarray, hr_h: int, hr_w: int, rho: int) -> np.ndarray:
+    """U[r, c] = bilinear interpolation of x_lr at (r / rho, c / rho): LR
+    sample (m, n) sits at HR (rho*m, rho*n); past the last LR row or column
+    the last sample's value is kept."""
+    h, w, C = x_lr.shape
+    out = np.empty((hr_h, hr_w, C))
+    for r in range(hr_h):
+        y = r / rho
+        y0 = min(int(math.floor(y)), h - 1)
+        fy = y - y0 if y0 < h - 1 else 0.0
+        y1 = min(y0 + 1, h - 1)
+        for c in range(hr_w):
+            x = c / rho
+            x0 = min(int(math.floor(x)), w - 1)
+            fx = x - x0 if x0 < w - 1 else 0.0
+            x1 = min(x0 + 1, w - 1)
+            out[r, c] = ((1 - fy) * ((1 - fx) * x_lr[y0, x0] + fx * x_lr[y0, x1]) +
+                         fy * ((1 - fx) * x_lr[y1, x0] + fx * x_lr[y1, x1]))
+    return out
+
+
+def sharpen_unsharp(u: np.ndarray, strength: float) -> np.ndarray:
+    """Unsharp masking u + s * (u - blur(u)), blur = 3x3 binomial kernel
+    (outer product of [1, 2, 1] / 4) with replicated edges."""
+    H, W, _ = u.shape
+    b = (0.25, 0.5, 0.25)
+    blur = np.zeros_like(u, dtype=np.float64)
+    for dy in (-1, 0, 1):
+        rows = np.clip(np.arange(H) + dy, 0, H - 1)
+        for dx in (-1, 0, 1):
+            cols = np.clip(np.arange(W) + dx, 0, W - 1)
+            blur += b[dy + 1] * b[dx + 1] * u[rows][:, cols]
+    return u + strength * (u - blur)
+
+
+def warm_start(x_lr: np.ndarray, noise: np.ndarray, rho: int, alpha: float, strength: float) -> np.ndarray:
+    """HR start latent at normalised time alpha = t/T for one image."""
+    hr_h, hr_w, _ = noise.shape
+    ref = sharpen_unsharp(upsample_bilinear(x_lr, hr_h, hr_w, rho), strength)
+    return alpha * noise + (1.0 - alpha) * ref
