@@ -19,7 +19,9 @@ For bf16 workloads the line also carries "backward": the training layer's
 backward step (permute dO, attention backward, RoPE transpose, unpermute dQ,
 dK, dV) after a forward that saved the LSE, with the attention backward's
 effective TFLOP/s counted as 10 * D * pairs * heads (the five products S,
-dP, dV, dK, dQ of the allowed pairs).
+dP, dV, dK, dQ of the allowed pairs).  "warm_start" times the warm-start
+kernel (once per image, not part of the step) on 256x256 x 64-channel bf16
+latents, batch 1 and 16, against HBM bandwidth.
 """
 from __future__ import annotations
 
@@ -94,6 +96,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward step measurement")
+    ap.add_argument("--no-warm", action="store_true", help="skip the warm-start kernel measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -113,8 +116,8 @@ def main():
     t_plan = time.perf_counter() - t_plan
     info = plan.info
 
-    def to_dev(a):
-        if w.dtype == "bf16":
+    def to_dev(a, dtype=None):
+        if (dtype or w.dtype) == "bf16":
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
@@ -214,6 +217,29 @@ def main():
         }
         del train, grads, d_o
 
+    warm = None
+    if not args.no_warm:
+        warm = {}
+        for wname in ("warm_4k", "warm_4k_b16"):
+            ww = WL.WARM_WORKLOADS[wname]
+            x_lr = to_dev(WL.warm_storage(ww, WL.WARM_LR), ww.dtype)
+            noise = to_dev(WL.warm_storage(ww, WL.WARM_NOISE), ww.dtype)
+            x_hr = torch.empty_like(noise)
+
+            def step_warm(ev=None):
+                if ev is not None:
+                    ev[0].record(stream)
+                U.ug_warm_start(x_lr, noise, ww.rho, ww.alpha, ww.sharpen, x_hr)
+                if ev is not None:
+                    ev[1].record(stream)
+
+            _, wavg = timed(step_warm, 2, 20, 3)
+            wms = wavg(0, 1)
+            nbytes = 2 * noise.numel() * noise.element_size() + x_lr.numel() * x_lr.element_size()
+            warm[wname] = {"ms": round(wms, 4), "bytes": nbytes, "gbs": round(nbytes / (wms * 1e-3) / 1e9, 1),
+                           "frac_hbm": round(nbytes / (wms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            del x_lr, noise, x_hr
+
     esize = 2 if w.dtype == "bf16" else 4
     tbytes = w.batch * w.seq_len * w.heads * w.head_dim * esize
     rope_bytes = 2 * 2 * w.batch * (w.n_hr + w.n_lr) * w.heads * w.head_dim * esize
@@ -264,6 +290,7 @@ def main():
             "unpermute_o": hbm(2 * tbytes, ums_unperm),
         },
         "backward": backward,
+        "warm_start": warm,
         "plan_build_s": round(t_plan, 4),
         "kernel_sha": kernel_hash(),
     }

@@ -22,7 +22,7 @@ UG_PLAN_HOST_ONLY = 1
 EXPORTED = ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr", "ug_permute",
             "ug_unpermute",
             "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_attn_fwd_lse", "ug_attn_bwd",
-            "ug_rope2d_bwd", "ug_status_str", "ug_last_error")
+            "ug_rope2d_bwd", "ug_warm_start", "ug_status_str", "ug_last_error")
 
 
 class UgDesc(ctypes.Structure):
@@ -30,6 +30,12 @@ class UgDesc(ctypes.Structure):
                 ("hr_w", c_int32), ("lr_h", c_int32), ("lr_w", c_int32), ("n_text", c_int32),
                 ("window", c_int32), ("radius", c_int32), ("rho", c_int32), ("dtype", c_int32),
                 ("flags", c_int32), ("lr_mode", c_int32), ("rope_theta", c_double)]
+
+
+class UgWarmDesc(ctypes.Structure):
+    _fields_ = [("batch", c_int32), ("hr_h", c_int32), ("hr_w", c_int32), ("lr_h", c_int32), ("lr_w", c_int32),
+                ("channels", c_int32), ("rho", c_int32), ("dtype", c_int32), ("alpha", ctypes.c_float),
+                ("sharpen", ctypes.c_float)]
 
 
 class UgInfo(ctypes.Structure):
@@ -72,6 +78,7 @@ def lib():
         L.ug_attn_fwd_lse.argtypes = [c_void_p] * 8
         L.ug_attn_bwd.argtypes = [c_void_p] * 12
         L.ug_rope2d_bwd.argtypes = [c_void_p] * 4
+        L.ug_warm_start.argtypes = [POINTER(UgWarmDesc), c_void_p, c_void_p, c_void_p, c_void_p]
         L.ug_status_str.argtypes = [c_int32]
         L.ug_status_str.restype = c_char_p
         L.ug_last_error.argtypes = []
@@ -79,7 +86,7 @@ def lib():
         for name in ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr", "ug_permute",
                      "ug_unpermute",
                      "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_attn_fwd_lse",
-                     "ug_attn_bwd", "ug_rope2d_bwd"):
+                     "ug_attn_bwd", "ug_rope2d_bwd", "ug_warm_start"):
             getattr(L, name).restype = c_int32
         _lib = L
     return _lib
@@ -328,6 +335,31 @@ def ug_rope2d_bwd(plan: Plan, dq_perm, dk_perm):
     _check("ug_rope2d_bwd", lib().ug_rope2d_bwd(plan.handle, c_void_p(dq_perm.data_ptr()),
                                                 c_void_p(dk_perm.data_ptr()), _stream_ptr(dq_perm)))
     return dq_perm, dk_perm
+
+
+def ug_warm_start(x_lr, noise, rho: int, alpha: float, sharpen: float, x_hr=None):
+    """HR start latent alpha * noise + (1 - alpha) * sharpen(upsample(x_lr));
+    x_lr [B, h, w, C] and noise [B, H, W, C] CUDA tensors of one dtype
+    (float32 or bfloat16), channels last.  x_hr may be `noise` (in place)."""
+    torch = _torch()
+    if x_lr.dtype != noise.dtype or x_lr.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x_lr and noise must share a dtype, float32 or bfloat16")
+    if x_lr.dim() != 4 or noise.dim() != 4 or x_lr.shape[0] != noise.shape[0] or x_lr.shape[3] != noise.shape[3]:
+        raise ValueError(f"expected x_lr [B, h, w, C] and noise [B, H, W, C], got {tuple(x_lr.shape)}, "
+                         f"{tuple(noise.shape)}")
+    if x_hr is None:
+        x_hr = torch.empty_like(noise)
+    for t, n in ((x_lr, "x_lr"), (noise, "noise"), (x_hr, "x_hr")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n}: expected a contiguous CUDA tensor")
+    if x_hr.shape != noise.shape or x_hr.dtype != noise.dtype:
+        raise ValueError("x_hr must match noise in shape and dtype")
+    B, H, W, C = noise.shape
+    d = UgWarmDesc(batch=B, hr_h=H, hr_w=W, lr_h=x_lr.shape[1], lr_w=x_lr.shape[2], channels=C, rho=rho,
+                   dtype=UG_BF16 if noise.dtype == torch.bfloat16 else UG_F32, alpha=alpha, sharpen=sharpen)
+    _check("ug_warm_start", lib().ug_warm_start(byref(d), c_void_p(x_lr.data_ptr()), c_void_p(noise.data_ptr()),
+                                                c_void_p(x_hr.data_ptr()), _stream_ptr(noise)))
+    return x_hr
 
 
 class TrainLayer:

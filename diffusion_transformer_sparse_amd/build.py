@@ -3,7 +3,8 @@
     python -m diffusion_transformer_sparse_amd.build
 
 Compiles csrc/plan.cpp (host) and the gfx950 device code (csrc/kernels.hip:
-layout, RoPE and attention forward; csrc/attn_bwd.hip: attention backward)
+layout, RoPE and attention forward; csrc/attn_bwd.hip: attention backward;
+csrc/warm_start.hip: the warm-start latent)
 with hipcc and links them into diffusion_transformer_sparse_amd/libultragen.so.
 All device code is built with packed-fp32 instructions disabled.
 """
@@ -22,7 +23,7 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + os.path.join(ROOT, "include"), "-I/opt/rocm/include"]
-DEVICE_SOURCES = ("kernels.hip", "attn_bwd.hip")
+DEVICE_SOURCES = ("kernels.hip", "attn_bwd.hip", "warm_start.hip")
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
 

@@ -246,6 +246,38 @@ ug_status ug_attn_bwd(ug_plan_t plan, const void* q, const void* k, const void* 
                       void* stream);
 ug_status ug_rope2d_bwd(ug_plan_t plan, void* dq_perm, void* dk_perm, void* stream);
 
+/*
+ * Guidance-weighted warm start (关键设计 4; gist.science summary 2.C): the HR
+ * sampler starts at normalised time alpha = t/T from
+ *   x_hr = alpha * noise + (1 - alpha) * Y,
+ *   Y = U + sharpen * (U - B*U),  U = bilinear upsampling of x_lr,
+ * where LR sample (m, n) sits at HR (rho*m, rho*n) (the coordinate map of
+ * 关键设计 2; past the last LR row/column the last sample's value is kept),
+ * and B is the 3x3 binomial blur ([1 2 1]/4 in each direction, edges
+ * replicated).  The pages name interpolation and sharpening without fixing
+ * them; these are the plainest linear choices.  noise is the caller's
+ * Gaussian draw X_T (the library draws no random numbers).
+ *  - x_lr:  [batch, lr_h, lr_w, channels], noise and x_hr: [batch, hr_h,
+ *    hr_w, channels]; contiguous, channels innermost (latent tokens in raster
+ *    order, as the attention's HR rows), dtype fp32 or bf16, 16-byte aligned;
+ *    channels a multiple of 4 (fp32) or 8 (bf16).
+ *  - fp32 arithmetic, one RNE rounding of the bf16 output.
+ *  - x_hr may be noise itself (in place); any other overlap is an error.
+ *  - Stateless: no plan; nothing is allocated.
+ */
+typedef struct ug_warm_desc {
+  int32_t batch;
+  int32_t hr_h, hr_w;
+  int32_t lr_h, lr_w;
+  int32_t channels;
+  int32_t rho;
+  int32_t dtype;  /* ug_dtype */
+  float alpha;    /* t / T, in [0, 1] */
+  float sharpen;  /* unsharp-mask strength, >= 0 (0: none) */
+} ug_warm_desc;
+
+ug_status ug_warm_start(const ug_warm_desc* desc, const void* x_lr, const void* noise, void* x_hr, void* stream);
+
 const char* ug_status_str(ug_status s);
 const char* ug_last_error(void);
 

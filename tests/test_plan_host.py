@@ -143,3 +143,30 @@ def test_block_order_covers_every_task_once():
     info = p.info
     assert info["attn_blocks"] >= info["attn_tasks"] * w.heads
     assert info["attn_blocks"] - info["attn_tasks"] * w.heads < 8 * 64
+
+
+@pytest.mark.parametrize("field,value", [("batch", 0), ("hr_h", 0), ("lr_w", 0), ("rho", 0), ("channels", 12),
+                                         ("channels", 0), ("dtype", 5), ("alpha", 1.5), ("alpha", -0.1),
+                                         ("alpha", float("nan")), ("sharpen", -1.0), ("sharpen", float("inf"))])
+def test_warm_start_descriptor_validation(field, value):
+    """Invalid warm-start descriptors are rejected before any HIP call."""
+    d = U.UgWarmDesc(batch=1, hr_h=16, hr_w=16, lr_h=4, lr_w=4, channels=16, rho=4, dtype=U.UG_BF16, alpha=0.5,
+                     sharpen=0.5)
+    setattr(d, field, value)
+    st = U.lib().ug_warm_start(ctypes.byref(d), ctypes.c_void_p(16), ctypes.c_void_p(4096),
+                               ctypes.c_void_p(1 << 20), None)
+    assert st == 1 and "ug_warm_start" in U.ug_last_error()
+
+
+def test_warm_start_rejects_overlap_and_null():
+    d = U.UgWarmDesc(batch=1, hr_h=16, hr_w=16, lr_h=4, lr_w=4, channels=16, rho=4, dtype=U.UG_BF16, alpha=0.5,
+                     sharpen=0.5)
+    lib = U.lib()
+    assert lib.ug_warm_start(None, None, None, None, None) == 1
+    assert lib.ug_warm_start(ctypes.byref(d), None, ctypes.c_void_p(4096), ctypes.c_void_p(1 << 20), None) == 1
+    # x_hr starting inside noise (partial overlap)
+    assert lib.ug_warm_start(ctypes.byref(d), ctypes.c_void_p(16), ctypes.c_void_p(1 << 20),
+                             ctypes.c_void_p((1 << 20) + 256), None) == 1
+    # x_hr overlapping x_lr
+    assert lib.ug_warm_start(ctypes.byref(d), ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 24),
+                             ctypes.c_void_p((1 << 20) - 4096), None) == 1

@@ -149,3 +149,57 @@ def tensor_storage(w: Workload, tensor: int, threads: int = 8) -> np.ndarray:
 
 def storage_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     return a.astype(np.float64) if dtype == "f32" else bf16_bits_to_f64(a)
+
+
+# --------------------------------------------------------------------------
+# Warm-start latents: channels-last [B, H, W, C] latent grids (C = 64 as in
+# FLUX's packed latent tokens; the pages do not state it).  x_lr and the noise
+# X_T are independent N(0, 1) draws, seeded [2026, cfg_id, 10 or 11, batch].
+# --------------------------------------------------------------------------
+WARM_LR, WARM_NOISE = 10, 11
+
+
+@dataclass(frozen=True)
+class WarmWorkload:
+    name: str
+    cfg_id: int
+    batch: int
+    hr_h: int
+    hr_w: int
+    lr_h: int
+    lr_w: int
+    channels: int
+    rho: int
+    dtype: str
+    alpha: float = 0.6    # t / T
+    sharpen: float = 0.5
+
+    def with_(self, **kw) -> "WarmWorkload":
+        d = asdict(self)
+        d.update(kw)
+        return WarmWorkload(**d)
+
+
+WARM_WORKLOADS = {
+    "warm_tiny": WarmWorkload("warm_tiny", 30, 1, 40, 36, 10, 9, 8, 4, "f32"),
+    "warm_ragged": WarmWorkload("warm_ragged", 31, 2, 250, 380, 63, 95, 64, 4, "bf16"),
+    "warm_4k": WarmWorkload("warm_4k", 32, 1, 256, 256, 64, 64, 64, 4, "bf16"),
+    "warm_4k_b16": WarmWorkload("warm_4k_b16", 33, 16, 256, 256, 64, 64, 64, 4, "bf16"),
+}
+
+
+def warm_storage(w: WarmWorkload, tensor: int) -> np.ndarray:
+    """x_lr [B, h, w, C] (tensor WARM_LR) or noise [B, H, W, C] (WARM_NOISE) in
+    storage form (float32, or uint16 bf16 bits)."""
+    hh, ww = (w.lr_h, w.lr_w) if tensor == WARM_LR else (w.hr_h, w.hr_w)
+    out = []
+    for b in range(w.batch):
+        x = np.random.default_rng([2026, w.cfg_id, tensor, b]).standard_normal((hh, ww, w.channels))
+        x32 = x.astype(np.float32)
+        out.append(x32 if w.dtype == "f32" else _round_f32_to_bf16_bits(x32))
+    return np.stack(out)
+
+
+def warm_f64(w: WarmWorkload, tensor: int) -> np.ndarray:
+    a = warm_storage(w, tensor)
+    return a.astype(np.float64) if w.dtype == "f32" else bf16_bits_to_f64(a)
