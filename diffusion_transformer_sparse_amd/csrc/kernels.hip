@@ -276,7 +276,7 @@ __global__ __launch_bounds__(1024) void permute_rope_kernel(const T* __restrict_
 // One workgroup = one query tile (<= 256 permuted rows sharing one key set)
 // of one (batch, head); 8 waves x 32 queries, two waves per SIMD.  The key
 // set is a list of contiguous row ranges, walked in 64-key tiles that go
-// straight from global memory into LDS (global_load_lds_dwordx4, no
+// straight from global memory into LDS (buffer_load_dwordx4 ... lds, no
 // registers), one barrier per tile.
 //
 // Per wave and 64-key tile, with 32x32 MFMA tiles (lane l: column l%32,
@@ -384,15 +384,13 @@ struct TileLoader {
     if (nv == kKT) {
 #pragma unroll
       for (int i = 0; i < Lds::kLoadsPerThread; ++i)
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(base + off[i]),
-                                         (lds_void*)(tile + (i * kAttnThreads + wave * 64) * 16), 16, 0, 0);
+        load_lds<16>(base, off[i], (lds_void*)(tile + (i * kAttnThreads + wave * 64) * 16));
     } else {
 #pragma unroll
       for (int i = 0; i < Lds::kLoadsPerThread; ++i) {
         const int r = min(row_of(i, tid), nv - 1);
-        const char* gp = base + int64_t(r) * rs * int64_t(sizeof(T)) + lchunk_of(i, tid) * 16;
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(gp),
-                                         (lds_void*)(tile + (i * kAttnThreads + wave * 64) * 16), 16, 0, 0);
+        const uint32_t o = uint32_t(int64_t(r) * rs * int64_t(sizeof(T)) + lchunk_of(i, tid) * 16);
+        load_lds<16>(base, o, (lds_void*)(tile + (i * kAttnThreads + wave * 64) * 16));
       }
     }
   }
