@@ -43,10 +43,13 @@ __device__ __forceinline__ float pair_sum(float x) {
 // and keep the global form.)
 constexpr int kBufferFlags = 0x00020000;
 
+// Lanes whose voffset + size exceeds `bytes` read zeros instead (the buffer
+// bounds check), which no lane can fault on.
 template <int kSize>
-__device__ __forceinline__ void load_lds(const void* row_base, uint32_t voffset, lds_void* lds_base) {
+__device__ __forceinline__ void load_lds(const void* row_base, uint32_t voffset, lds_void* lds_base,
+                                         int32_t bytes = 0x7fffffff) {
   const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row_base), (short)0, 0x7fffffff, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row_base), (short)0, bytes, kBufferFlags);
   static_assert(kSize == 16 || kSize == 4, "16- or 4-byte lanes");
   if constexpr (kSize == 16)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_base, 16, voffset, 0, 0, 0);
@@ -56,14 +59,17 @@ __device__ __forceinline__ void load_lds(const void* row_base, uint32_t voffset,
 
 // Walks the 64-row tiles of a list of row ranges (key ranges of a query
 // tile, or query ranges of a key tile), one range after another.
+// The cursor is wave-uniform; the range bounds are read back with
+// readfirstlane so the compiler knows it (they feed scalar buffer
+// descriptors).
 struct TileCursor {
   int32_t ri, r1, ks, k1;
   __device__ __forceinline__ void init(const ug::Range* ranges, int32_t r0, int32_t rend) {
     ri = r0;
     r1 = rend;
     const ug::Range r = ranges[r0];
-    ks = r.k0;
-    k1 = r.k1;
+    ks = __builtin_amdgcn_readfirstlane(r.k0);
+    k1 = __builtin_amdgcn_readfirstlane(r.k1);
   }
   __device__ __forceinline__ int32_t nv() const { return min(ug::kAttnKeyTile, k1 - ks); }
   __device__ __forceinline__ void advance(const ug::Range* ranges) {
@@ -71,8 +77,8 @@ struct TileCursor {
     if (ks >= k1 && ri + 1 < r1) {
       ++ri;
       const ug::Range r = ranges[ri];
-      ks = r.k0;
-      k1 = r.k1;
+      ks = __builtin_amdgcn_readfirstlane(r.k0);
+      k1 = __builtin_amdgcn_readfirstlane(r.k1);
     }
   }
 };

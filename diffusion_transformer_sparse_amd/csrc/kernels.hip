@@ -361,8 +361,10 @@ struct AttnLds {
 // s = i*512 + tid of the tile holds row s / kChunks, physical chunk
 // s % kChunks, i.e. logical chunk (s % kChunks) ^ swz(row).  `off[i]` is the
 // thread's byte offset of that chunk relative to row ks (constant over
-// tiles); a ragged tile (nv < 64) repeats its last row instead (those scores
-// are masked), so no load leaves the key range.
+// tiles).  The buffer descriptor covers the nv valid rows only, so in a
+// ragged tile (nv < 64) the rows past the range read as zeros (their scores
+// are masked and their P is 0) and no load leaves the key range; nv <= 0
+// loads nothing but zeros.  The issue is branch-free.
 template <typename T, int D, bool kIsV>
 struct TileLoader {
   using Lds = AttnLds<T, D>;
@@ -381,18 +383,12 @@ struct TileLoader {
   __device__ __forceinline__ void issue(const T* __restrict__ src, int64_t rs, int32_t ks, int32_t nv, char* tile,
                                         int tid, int wave) const {
     const char* base = reinterpret_cast<const char*>(src + int64_t(ks) * rs);  // wave-uniform
-    if (nv == kKT) {
+    // uniform by construction; readfirstlane keeps the descriptor in scalar registers
+    const int32_t bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * int32_t(rs) * int32_t(sizeof(T)));
 #pragma unroll
-      for (int i = 0; i < Lds::kLoadsPerThread; ++i)
-        load_lds<16>(base, off[i], (lds_void*)(tile + (i * kAttnThreads + wave * 64) * 16));
-    } else {
-#pragma unroll
-      for (int i = 0; i < Lds::kLoadsPerThread; ++i) {
-        const int r = min(row_of(i, tid), nv - 1);
-        const uint32_t o = uint32_t(int64_t(r) * rs * int64_t(sizeof(T)) + lchunk_of(i, tid) * 16);
-        load_lds<16>(base, o, (lds_void*)(tile + (i * kAttnThreads + wave * 64) * 16));
-      }
-    }
+    for (int i = 0; i < Lds::kLoadsPerThread; ++i)
+      load_lds<16>(base, off[i], (lds_void*)(tile + (i * kAttnThreads + wave * 64) * 16), bytes);
+    (void)tid;
   }
 };
 
@@ -475,6 +471,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
     const ug::Range rg = s_rng[r];
     ntiles += (rg.k1 - rg.k0 + kKT - 1) / kKT;
   }
+  ntiles = __builtin_amdgcn_readfirstlane(ntiles);  // uniform: it feeds scalar buffer descriptors
 
   // Per-lane LDS byte offsets.  K operand of step i: row l32 (plus 32 per
   // block), logical chunk of dims (16i + 8g) [bf16] or element 2i + g [fp32].
