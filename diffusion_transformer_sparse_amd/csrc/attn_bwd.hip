@@ -264,6 +264,8 @@ struct BwdParams {
   const ug::Task* tasks;
   const ug::Range* ranges;
   const ug::Block* blocks;
+  const int32_t* mask_off;  // dK/dV pass: per key tile, offset of its key masks, or < 0
+  const uint64_t* masks;    // bit r: the key row sees the tile's query range r
   float scale_log2;  // log2(e) / sqrt(D)
   float scale;       // 1 / sqrt(D)
 };
@@ -401,6 +403,10 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
 
   const int32_t nr = task.r1 - task.r0;
   if (tid < nr) s_rng[tid] = p.ranges[task.r0 + tid];
+  // Which of the tile's query ranges this lane's key sees (all of them
+  // unless the tile groups corresponding-LR windows).
+  const int32_t moff = p.mask_off ? p.mask_off[blk.task] : -1;  // uniform
+  const uint64_t kmask = moff >= 0 ? p.masks[moff + (kload - task.q0)] : ~uint64_t(0);
 
   bf16x8 kf[D / 16];
   char* const vblk = smem + 4 * TB + 2 * SB + wave * VB;
@@ -439,6 +445,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
   for (int t = 0; t < D / 32; ++t) dka[t] = dva[t] = f32x16{};
 
   int32_t nv = cur.nv();
+  int32_t rcur = cur.ri;  // query range (index into the tile's ranges) of the tile being processed
   ld.issue(qg, rs, cur.ks, nv, smem, tid, wave);
   ld.issue(dog, rs, cur.ks, nv, smem + 2 * TB, tid, wave);
   issue_stats(cur.ks, smem + 4 * TB);
@@ -449,6 +456,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
   for (int32_t i = 0; i < ntiles; ++i) {
     const int slot = i & 1;
     const int32_t nv_next = cur.nv();
+    const int32_t rnext = cur.ri;
     if (i + 1 < ntiles) {
       ld.issue(qg, rs, cur.ks, nv_next, smem + (slot ^ 1) * TB, tid, wave);
       ld.issue(dog, rs, cur.ks, nv_next, smem + 2 * TB + (slot ^ 1) * TB, tid, wave);
@@ -458,8 +466,15 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
     const char* qt = smem + slot * TB;
     const char* dot = smem + 2 * TB + slot * TB;
     const float* st = reinterpret_cast<const float*>(smem + 4 * TB + slot * SB);
+    // Query rows at or past `lim` contribute nothing to this lane's key: the
+    // ragged tail of the tile, or all rows when the key does not see the range.
+    const bool sees = (kmask >> rcur) & 1;
+    const uint64_t seen = __ballot(sees);
+    const int32_t lim = sees ? nv : 0;
+    const bool full = nv == kRows && seen == ~uint64_t(0);  // uniform
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
+      if (seen == 0) break;  // no key of this wave sees the range (uniform)
       const f32x16 s = rows_x_regs<D>(qt, mb, kf, lo);
       const f32x16 dp = rows_x_rows<D>(dot, mb, vblk, lo);
       // one 16-query chunk (registers 8cc .. 8cc+7) at a time: P and dS of
@@ -479,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
           for (int e = 0; e < 4; ++e) {
             const int j = 4 * a + e;
             float pv = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -lv[e]));
-            if (nv < kRows && row0 + e >= nv) pv = 0.f;
+            if (!full && row0 + e >= lim) pv = 0.f;
             pb[4 * a2 + e] = __bf16(pv);
             dsb[4 * a2 + e] = __bf16(pv * (dp[j] - dl[e]));
           }
@@ -497,6 +512,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
       }
     }
     nv = nv_next;
+    rcur = rnext;
     __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of the next tile have landed
     __syncthreads();
   }
@@ -519,6 +535,8 @@ void launch_bwd(ug_plan_t p, BwdParams bp, const __bf16* o, const float* lse, fl
   bp.tasks = p->d_ktasks;
   bp.ranges = p->d_kranges;
   bp.blocks = p->d_kblocks;
+  bp.mask_off = p->d_kmask_off;
+  bp.masks = p->d_kmasks;
   if (!p->kblocks.empty())
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3(unsigned(p->kblocks.size())), dim3(kThreads), 0, s, bp);
 }

@@ -253,10 +253,73 @@ void build_tasks(ug_plan_s& p) {
 // neighbourhood relation is symmetric); LR keys by the HR queries (all of
 // them, or with lr_mode 1 those of the windows around the anchor's window)
 // and by every LR query.  The transposed pair count must equal the forward's.
+// Corresponding-LR key tiles (lr_mode 1).  The anchors of LR window u are
+// seen by the LR rows and by the HR rows of the windows around u.  One
+// window holds only (l/rho)^2 anchors (16 at l = 16, rho = 4), so a key tile
+// per window would leave most of a 256-key workgroup idle.  Consecutive
+// windows are grouped instead (up to 256 keys, as long as 1 + the number of
+// HR windows around any of them stays within kAttnMaxRanges): the tile's
+// query ranges are the LR rows (range 0) and each HR window around the
+// group (ranges 1..), unmerged, and each key carries the bit mask of the
+// ranges it sees.
+void add_lr_key_groups(ug_plan_s& p) {
+  const int32_t T = int32_t(p.T), N = int32_t(p.N), L = int32_t(p.L);
+  auto around = [&](int u) {  // sorted
+    std::vector<int32_t> a(p.nbr.begin() + p.nbr_off[u], p.nbr.begin() + p.nbr_off[u + 1]);
+    std::sort(a.begin(), a.end());
+    return a;
+  };
+  auto united = [](std::vector<int32_t> a, const std::vector<int32_t>& b) {
+    a.insert(a.end(), b.begin(), b.end());
+    std::sort(a.begin(), a.end());
+    a.erase(std::unique(a.begin(), a.end()), a.end());
+    return a;
+  };
+  for (int w = 0; w < p.nwin;) {
+    std::vector<int32_t> hr = around(w);
+    int w1 = w + 1;
+    int32_t keys = p.lr_win_off[w1] - p.lr_win_off[w];
+    while (w1 < p.nwin) {
+      const int32_t kw = p.lr_win_off[w1 + 1] - p.lr_win_off[w1];
+      std::vector<int32_t> cand = united(hr, around(w1));
+      if (keys + kw > kAttnQueryTile || 1 + int32_t(cand.size()) > kAttnMaxRanges) break;
+      hr.swap(cand);
+      keys += kw;
+      ++w1;
+    }
+    const int32_t q0 = T + N + p.lr_win_off[w], q1 = T + N + p.lr_win_off[w1];
+    if (q1 > q0 && 1 + int32_t(hr.size()) <= kAttnMaxRanges) {
+      const int32_t r0 = int32_t(p.kranges.size());
+      p.kranges.push_back({T + N, L});
+      for (int32_t v : hr) p.kranges.push_back({T + p.win_off[v], T + p.win_off[v + 1]});
+      const int32_t r1 = int32_t(p.kranges.size());
+      const int32_t m0 = int32_t(p.kmasks.size());
+      for (int u = w; u < w1; ++u) {
+        const std::vector<int32_t> nu = around(u);
+        uint64_t bits = 1;  // the LR rows
+        for (size_t j = 0; j < hr.size(); ++j)
+          if (std::binary_search(nu.begin(), nu.end(), hr[j])) bits |= uint64_t(1) << (j + 1);
+        for (int32_t k = p.lr_win_off[u]; k < p.lr_win_off[u + 1]; ++k) p.kmasks.push_back(bits);
+      }
+      for (int32_t q = q0; q < q1; q += kAttnQueryTile) {
+        p.ktasks.push_back({q, std::min(q1, q + kAttnQueryTile), r0, r1});
+        p.kmask_off.push_back(m0 + (q - q0));
+      }
+    } else if (q1 > q0) {  // one window whose neighbourhood alone exceeds the range limit: plain tiles
+      std::vector<ug::Range> rs{{T + N, L}};
+      for (int32_t v : around(w)) rs.push_back({T + p.win_off[v], T + p.win_off[v + 1]});
+      add_tasks(p.ktasks, p.kranges, q0, q1, rs);
+      p.kmask_off.resize(p.ktasks.size(), -1);
+    }
+    w = w1;
+  }
+}
+
 void build_key_tasks(ug_plan_s& p) {
   const int32_t T = int32_t(p.T), N = int32_t(p.N), L = int32_t(p.L);
   p.ktasks.clear();
   p.kranges.clear();
+  p.kmasks.clear();
   auto hr_runs_around = [&](int w, std::vector<ug::Range>& rs) {
     for (int e = p.nbr_off[w]; e < p.nbr_off[w + 1]; ++e) {
       const int v = p.nbr[e];
@@ -271,16 +334,28 @@ void build_key_tasks(ug_plan_s& p) {
     add_tasks(p.ktasks, p.kranges, T + p.win_off[w], T + p.win_off[w + 1], rs);
   }
   if (p.Nlr > 0 && p.d.lr_mode == 0) add_tasks(p.ktasks, p.kranges, T + N, L, {{T, L}});
+  p.kmask_off.assign(p.ktasks.size(), -1);
   if (p.Nlr > 0 && p.d.lr_mode == 1) {
-    for (int w = 0; w < p.nwin; ++w) {
-      std::vector<ug::Range> rs{{T + N, L}};
-      hr_runs_around(w, rs);
-      add_tasks(p.ktasks, p.kranges, T + N + p.lr_win_off[w], T + N + p.lr_win_off[w + 1], rs);
-    }
+    add_lr_key_groups(p);
     add_tasks(p.ktasks, p.kranges, T + N + p.lr_win_off[p.nwin], L, {{T + N, L}});
+    p.kmask_off.resize(p.ktasks.size(), -1);
   }
-  int64_t pairs = 0, tiles = 0;
-  count_tasks(p.ktasks, p.kranges, &pairs, &tiles, &p.kmax_task_ranges);
+  // allowed pairs, honouring the key masks
+  int64_t pairs = 0;
+  p.kmax_task_ranges = 0;
+  for (size_t t = 0; t < p.ktasks.size(); ++t) {
+    const ug::Task& kt = p.ktasks[t];
+    p.kmax_task_ranges = std::max(p.kmax_task_ranges, kt.r1 - kt.r0);
+    for (int r = kt.r0; r < kt.r1; ++r) {
+      const int64_t len = p.kranges[r].k1 - p.kranges[r].k0;
+      if (p.kmask_off[t] < 0) {
+        pairs += int64_t(kt.q1 - kt.q0) * len;
+        continue;
+      }
+      for (int32_t j = 0; j < kt.q1 - kt.q0; ++j)
+        if ((p.kmasks[p.kmask_off[t] + j] >> (r - kt.r0)) & 1) pairs += len;
+    }
+  }
   if (pairs != p.pairs) throw std::logic_error("transposed mask pair count differs from the forward's");
 }
 
@@ -356,8 +431,9 @@ ug_status upload(const std::vector<T>& h, T** d) {
 }
 
 void free_device(ug_plan_s* p) {
-  void* ptrs[] = {p->d_perm,  p->d_inv,    p->d_lr_perm, p->d_lr_inv,  p->d_rope,
-                  p->d_tasks, p->d_ranges, p->d_blocks,  p->d_ktasks, p->d_kranges, p->d_kblocks};
+  void* ptrs[] = {p->d_perm,    p->d_inv,     p->d_lr_perm, p->d_lr_inv,     p->d_rope,
+                  p->d_tasks,   p->d_ranges,  p->d_blocks,  p->d_ktasks,     p->d_kranges,
+                  p->d_kblocks, p->d_kmasks, p->d_kmask_off};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
   p->d_perm = p->d_inv = nullptr;
@@ -369,6 +445,8 @@ void free_device(ug_plan_s* p) {
   p->d_ktasks = nullptr;
   p->d_kranges = nullptr;
   p->d_kblocks = nullptr;
+  p->d_kmasks = nullptr;
+  p->d_kmask_off = nullptr;
 }
 
 ug_status check_device(ug_plan_s* p) {
@@ -437,6 +515,8 @@ ug_status ug_plan(const ug_desc* desc, ug_plan_t* out) {
     if (s == UG_OK) s = ug::upload(p->ktasks, &p->d_ktasks);
     if (s == UG_OK) s = ug::upload(p->kranges, &p->d_kranges);
     if (s == UG_OK) s = ug::upload(p->kblocks, &p->d_kblocks);
+    if (s == UG_OK) s = ug::upload(p->kmask_off, &p->d_kmask_off);
+    if (s == UG_OK) s = ug::upload(p->kmasks, &p->d_kmasks);
     if (s != UG_OK) {
       ug::free_device(p);
       delete p;

@@ -60,6 +60,12 @@ struct ug_plan_s {
   std::vector<ug::Range> kranges;
   std::vector<ug::Block> kblocks;
   int32_t kmax_task_ranges = 0;
+  // Key tiles that group several LR windows (lr_mode 1) see the union of
+  // their windows' query ranges; bit r of kmasks[kmask_off[t] + j] says
+  // whether key row ktasks[t].q0 + j sees the task's query range r.
+  // kmask_off[t] < 0: every key of the tile sees every range.
+  std::vector<int32_t> kmask_off;
+  std::vector<uint64_t> kmasks;
 
   // Backward statistics (log2-scaled LSE and Delta per row) live in the
   // caller's workspace as two [batch*heads][stat_rows] float arrays; the rows
@@ -80,6 +86,8 @@ struct ug_plan_s {
   ug::Task* d_ktasks = nullptr;
   ug::Range* d_kranges = nullptr;
   ug::Block* d_kblocks = nullptr;
+  int32_t* d_kmask_off = nullptr;
+  uint64_t* d_kmasks = nullptr;  // null when no key tile is masked
 };
 
 namespace ug {

@@ -200,6 +200,8 @@ EDGE_BWD = {
     "window_covers_grid": dict(window=64),
     "batch2": dict(batch=2),
     "corr_overhang": dict(lr_mode=1, lr_h=14, lr_w=14),
+    "corr_radius2": dict(lr_mode=1, radius=2),
+    "corr_window8": dict(lr_mode=1, window=8),
 }
 
 
@@ -231,14 +233,17 @@ def test_backward_is_deterministic(U):
 def test_full_size_backward_sampled(U, name):
     """The 256x256 layer's backward at full size; the oracle recomputes dq of
     sampled query rows (corner, edge, interior HR, text, LR) and dk, dv of
-    sampled HR key rows one by one."""
+    sampled HR key rows (with lr_mode 1 also LR key rows) one by one."""
     w = WL.WORKLOADS[name]
     _, (_, dq, dk, dv) = run_layer_bwd(U, w)
     geo = O.geometry_of(w)
     T, W = w.n_text, w.hr_w
     qrows = np.array([0, T - 1, T, T + 15 * W + 16, T + 100 * W + 37, T + w.n_hr - 1, T + w.n_hr,
                       w.seq_len - 1])
-    krows = np.array([T + 16 * W + 16, T + 255 * W + 3])
+    krows = [T + 16 * W + 16, T + 255 * W + 3]
+    if w.lr_mode == 1:  # an LR key is then seen by nine windows' queries, not all of them
+        krows += [T + w.n_hr, T + w.n_hr + 37 * w.lr_w + 5, w.seq_len - 1]
+    krows = np.array(krows)
     for h in (0, w.heads - 1):
         qh, kh, vh, doh = (WL.head_f64(w, t, h) for t in (WL.Q, WL.K, WL.V, WL.DO))
         rq = O.backward_query_rows(geo, qh, kh, vh, doh, w.rope_theta, qrows)
