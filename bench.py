@@ -16,10 +16,10 @@ pairs count.  Per-kernel times come from HIP events recorded on the stream
 the kernels are launched on (torch's current stream).
 
 For bf16 workloads the line also carries "backward": the training layer's
-backward step (permute dO, attention backward, RoPE transpose, unpermute dQ,
-dK, dV) after a forward that saved the LSE, with the attention backward's
-effective TFLOP/s counted as 10 * D * pairs * heads (the five products S,
-dP, dV, dK, dQ of the allowed pairs).  "warm_start" times the warm-start
+backward step (permute dO, attention backward, RoPE transpose and unpermute
+of dQ, dK in one pass, unpermute dV) after a forward that saved the LSE, with
+the attention backward's effective TFLOP/s counted as 10 * D * pairs * heads
+(the five products S, dP, dV, dK, dQ of the allowed pairs).  "warm_start" times the warm-start
 kernel (once per image, not part of the step) on 256x256 x 64-channel bf16
 latents, batch 1 and 16, against HBM bandwidth.
 """
@@ -198,9 +198,8 @@ def main():
                           train.dv, train.ws)
             if ev is not None:
                 ev[2].record(stream)
-            U.ug_rope2d_bwd(plan, train.dq, train.dk)
-            for src, dst in zip((train.dq, train.dk, train.dv), grads):
-                U.ug_unpermute(plan, src, dst)
+            U.ug_permute_rope_bwd(plan, train.dq, train.dk, grads[0], grads[1])
+            U.ug_unpermute(plan, train.dv, grads[2])
             if ev is not None:
                 ev[3].record(stream)
 
@@ -209,7 +208,7 @@ def main():
         bflops = 2.5 * info["eff_flops"]
         backward = {
             "ms_per_step": round(bms_step, 4),
-            "step": "ug_permute(dO) + ug_attn_bwd + ug_rope2d_bwd(dQ,dK) + ug_unpermute(dQ,dK,dV)",
+            "step": "ug_permute(dO) + ug_attn_bwd + ug_permute_rope_bwd(dQ,dK) + ug_unpermute(dV)",
             "attn_bwd": {"ms": round(bms_attn, 4), "eff_tflops": round(bflops / (bms_attn * 1e-3) / 1e12, 2),
                          "frac_peak": round(bflops / (bms_attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                          "eff_flop": bflops},

@@ -22,7 +22,7 @@ UG_PLAN_HOST_ONLY = 1
 EXPORTED = ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr", "ug_permute",
             "ug_unpermute",
             "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_attn_fwd_lse", "ug_attn_bwd",
-            "ug_rope2d_bwd", "ug_warm_start", "ug_status_str", "ug_last_error")
+            "ug_rope2d_bwd", "ug_permute_rope_bwd", "ug_warm_start", "ug_status_str", "ug_last_error")
 
 
 class UgDesc(ctypes.Structure):
@@ -78,6 +78,7 @@ def lib():
         L.ug_attn_fwd_lse.argtypes = [c_void_p] * 8
         L.ug_attn_bwd.argtypes = [c_void_p] * 12
         L.ug_rope2d_bwd.argtypes = [c_void_p] * 4
+        L.ug_permute_rope_bwd.argtypes = [c_void_p] * 6
         L.ug_warm_start.argtypes = [POINTER(UgWarmDesc), c_void_p, c_void_p, c_void_p, c_void_p]
         L.ug_status_str.argtypes = [c_int32]
         L.ug_status_str.restype = c_char_p
@@ -86,7 +87,7 @@ def lib():
         for name in ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr", "ug_permute",
                      "ug_unpermute",
                      "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_attn_fwd_lse",
-                     "ug_attn_bwd", "ug_rope2d_bwd", "ug_warm_start"):
+                     "ug_attn_bwd", "ug_rope2d_bwd", "ug_permute_rope_bwd", "ug_warm_start"):
             getattr(L, name).restype = c_int32
         _lib = L
     return _lib
@@ -337,6 +338,23 @@ def ug_rope2d_bwd(plan: Plan, dq_perm, dk_perm):
     return dq_perm, dk_perm
 
 
+def ug_permute_rope_bwd(plan: Plan, dq_perm, dk_perm, dq_raster=None, dk_raster=None):
+    """The transpose of ug_permute_rope: ug_rope2d_bwd followed by
+    ug_unpermute of dq and dk, in one pass, out of place."""
+    _check_tensor(plan, dq_perm, "dq_perm")
+    _check_tensor(plan, dk_perm, "dk_perm")
+    if dq_raster is None:
+        dq_raster = _torch().empty_like(dq_perm)
+    if dk_raster is None:
+        dk_raster = _torch().empty_like(dk_perm)
+    _check_tensor(plan, dq_raster, "dq_raster")
+    _check_tensor(plan, dk_raster, "dk_raster")
+    _check("ug_permute_rope_bwd", lib().ug_permute_rope_bwd(plan.handle, c_void_p(dq_perm.data_ptr()),
+                                                            c_void_p(dk_perm.data_ptr()), c_void_p(dq_raster.data_ptr()),
+                                                            c_void_p(dk_raster.data_ptr()), _stream_ptr(dq_perm)))
+    return dq_raster, dk_raster
+
+
 def ug_warm_start(x_lr, noise, rho: int, alpha: float, sharpen: float, x_hr=None):
     """HR start latent alpha * noise + (1 - alpha) * sharpen(upsample(x_lr));
     x_lr [B, h, w, C] and noise [B, H, W, C] CUDA tensors of one dtype
@@ -366,8 +384,8 @@ class TrainLayer:
     """Forward that keeps what the backward needs, and the backward of the
     whole layer (raster in, raster out):
       forward:  permute+RoPE Q, K; permute V; attention with LSE; unpermute O
-      backward: permute dO; attention backward; RoPE transpose on dQ, dK;
-                unpermute dQ, dK, dV."""
+      backward: permute dO; attention backward; RoPE transpose and unpermute
+                of dQ, dK in one pass; unpermute dV."""
 
     def __init__(self, plan: Plan, device="cuda"):
         torch = _torch()
@@ -390,9 +408,7 @@ class TrainLayer:
         p = self.plan
         ug_permute(p, d_out, self.dop)
         ug_attn_bwd(p, self.qp, self.kp, self.vp, self.op, self.dop, self.lse, self.dq, self.dk, self.dv, self.ws)
-        ug_rope2d_bwd(p, self.dq, self.dk)
-        ug_unpermute(p, self.dq, dq)
-        ug_unpermute(p, self.dk, dk)
+        ug_permute_rope_bwd(p, self.dq, self.dk, dq, dk)
         ug_unpermute(p, self.dv, dv)
         return dq, dk, dv
 

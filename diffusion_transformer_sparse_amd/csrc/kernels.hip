@@ -173,19 +173,26 @@ __global__ __launch_bounds__(1024) void rope2d_kernel(T* __restrict__ q, T* __re
 }
 
 // ---------------------------------------------------------------------------
-// Fused window-first permutation + 2D axial RoPE of Q and K: permuted row j
-// reads raster row map(j) of both tensors, rotates HR and LR rows exactly as
-// rope2d_kernel does (same table, same fp32 arithmetic, so the result is
-// bit-identical to permute followed by rope2d) and copies text rows as they
-// are.  One read and one write of Q and K instead of two of each.
+// Fused window-first permutation + 2D axial RoPE of Q and K, and its
+// transpose for the gradients.
+//   forward (kBwd false): permuted row j reads raster row T0 + perm[j - T0]
+//     (HR; LR through lr_perm) and rotates it by the position of that raster
+//     row;
+//   backward (kBwd true): raster row j reads permuted row T0 + inv[j - T0]
+//     (HR; LR through lr_inv) and applies the transposed rotation of raster
+//     row j's position.
+// HR and LR rows are rotated exactly as rope2d_kernel does (same table, same
+// fp32 arithmetic), so the result is bit-identical to permute followed by
+// rope2d, or to rope2d's transpose followed by unpermute; text rows are
+// copied.  One read and one write of Q and K instead of two of each.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool kBwd>
 __global__ __launch_bounds__(1024) void permute_rope_kernel(const T* __restrict__ qsrc, const T* __restrict__ ksrc,
                                                             T* __restrict__ qdst, T* __restrict__ kdst, int32_t L,
                                                             int32_t T0, int32_t N, int32_t W, int32_t lr_w,
                                                             int32_t rho, int32_t heads, int32_t D,
-                                                            const int32_t* __restrict__ perm,
-                                                            const int32_t* __restrict__ lr_perm,
+                                                            const int32_t* __restrict__ tab_hr,
+                                                            const int32_t* __restrict__ tab_lr,
                                                             const float2* __restrict__ cs) {
   constexpr int E = 16 / sizeof(T);
   const int32_t units_per_head = D / E;
@@ -204,13 +211,16 @@ __global__ __launch_bounds__(1024) void permute_rope_kernel(const T* __restrict_
     pr[r] = -1;  // text: not rotated
     pc[r] = 0;
     if (j >= T0 && j < T0 + N) {
-      const int32_t idx = perm[j - T0];
-      src[r] = T0 + idx;
+      const int32_t t = tab_hr[j - T0];
+      const int32_t idx = kBwd ? j - T0 : t;  // raster HR index of the rotated row
+      src[r] = T0 + t;
       pr[r] = idx / W;
       pc[r] = idx - pr[r] * W;
     } else if (j >= T0 + N) {
-      const int32_t i = lr_perm ? lr_perm[j - T0 - N] : j - T0 - N;  // raster LR index
-      src[r] = T0 + N + i;
+      const int32_t li = j - T0 - N;
+      const int32_t t = tab_lr ? tab_lr[li] : li;
+      const int32_t i = kBwd ? li : t;  // raster LR index of the rotated row
+      src[r] = T0 + N + t;
       const int32_t m = i / lr_w;
       pr[r] = rho * m;
       pc[r] = rho * (i - m * lr_w);
@@ -238,7 +248,7 @@ __global__ __launch_bounds__(1024) void permute_rope_kernel(const T* __restrict_
           float* y = reinterpret_cast<float*>(&ka[r]);
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
-            const float2 t = tab[p];
+            const float2 t = rot<kBwd>(tab[p]);
             const float a = x[2 * p], b = x[2 * p + 1];
             x[2 * p] = a * t.x - b * t.y;
             x[2 * p + 1] = a * t.y + b * t.x;
@@ -251,7 +261,7 @@ __global__ __launch_bounds__(1024) void permute_rope_kernel(const T* __restrict_
           bf16x8 y = *reinterpret_cast<bf16x8*>(&ka[r]);
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            const float2 t = tab[p];
+            const float2 t = rot<kBwd>(tab[p]);
             const float a = float(x[2 * p]), b = float(x[2 * p + 1]);
             x[2 * p] = __bf16(a * t.x - b * t.y);
             x[2 * p + 1] = __bf16(a * t.y + b * t.x);
@@ -842,6 +852,46 @@ ug_status rope_common(ug_plan_t p, void* q_perm, void* k_perm, void* stream, con
   return launch_status(fn);
 }
 
+template <bool kBwd>
+ug_status permute_rope_common(ug_plan_t p, const void* q_in, const void* k_in, void* q_out, void* k_out,
+                              void* stream, const char* fn) {
+  ug::clear_error();
+  ug_status st = check_plan(p, fn);
+  if (st != UG_OK) return st;
+  if (!q_in || !k_in || !q_out || !k_out) return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": NULL tensor");
+  if (!aligned16(q_in) || !aligned16(k_in) || !aligned16(q_out) || !aligned16(k_out))
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": tensors must be 16-byte aligned");
+  const int64_t n = tensor_bytes(p);
+  const void* ins[2] = {q_in, k_in};
+  const void* outs[2] = {q_out, k_out};
+  for (const void* a : outs)
+    for (const void* b : ins)
+      if (overlap(a, b, n)) return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": an output overlaps an input");
+  if (overlap(q_out, k_out, n)) return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": the two outputs overlap");
+  if (current_device() != p->device)
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": current device is not the plan's device");
+  const int E = p->d.dtype == UG_BF16 ? 8 : 4;
+  const int64_t units = int64_t(p->d.heads) * p->d.head_dim / E;
+  const dim3 grid(unsigned((p->L + kRopeRows - 1) / kRopeRows), unsigned(p->d.batch));
+  const unsigned threads = unsigned(std::min<int64_t>(1024, (units + 63) / 64 * 64));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float2* cs = reinterpret_cast<const float2*>(p->d_rope);
+  const int32_t lr_w = std::max(p->d.lr_w, 1);
+  const int32_t* tab_hr = kBwd ? p->d_inv : p->d_perm;
+  const int32_t* tab_lr = kBwd ? p->d_lr_inv : p->d_lr_perm;
+  if (p->d.dtype == UG_BF16)
+    hipLaunchKernelGGL((permute_rope_kernel<__bf16, kBwd>), grid, dim3(threads), 0, s,
+                       static_cast<const __bf16*>(q_in), static_cast<const __bf16*>(k_in), static_cast<__bf16*>(q_out),
+                       static_cast<__bf16*>(k_out), int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w,
+                       p->d.rho, p->d.heads, p->d.head_dim, tab_hr, tab_lr, cs);
+  else
+    hipLaunchKernelGGL((permute_rope_kernel<float, kBwd>), grid, dim3(threads), 0, s, static_cast<const float*>(q_in),
+                       static_cast<const float*>(k_in), static_cast<float*>(q_out), static_cast<float*>(k_out),
+                       int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w, p->d.rho, p->d.heads,
+                       p->d.head_dim, tab_hr, tab_lr, cs);
+  return launch_status(fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -885,40 +935,12 @@ ug_status ug_attn_fwd_lse(ug_plan_t p, const void* q, const void* k, const void*
 
 ug_status ug_permute_rope(ug_plan_t p, const void* q_raster, const void* k_raster, void* q_perm, void* k_perm,
                           void* stream) {
-  ug::clear_error();
-  ug_status st = check_plan(p, "ug_permute_rope");
-  if (st != UG_OK) return st;
-  if (!q_raster || !k_raster || !q_perm || !k_perm)
-    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_permute_rope: NULL tensor");
-  if (!aligned16(q_raster) || !aligned16(k_raster) || !aligned16(q_perm) || !aligned16(k_perm))
-    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_permute_rope: tensors must be 16-byte aligned");
-  const int64_t n = tensor_bytes(p);
-  const void* ins[2] = {q_raster, k_raster};
-  const void* outs[2] = {q_perm, k_perm};
-  for (const void* a : outs)
-    for (const void* b : ins)
-      if (overlap(a, b, n)) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_permute_rope: an output overlaps an input");
-  if (overlap(q_perm, k_perm, n)) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_permute_rope: q_perm and k_perm overlap");
-  if (current_device() != p->device)
-    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_permute_rope: current device is not the plan's device");
-  const int E = p->d.dtype == UG_BF16 ? 8 : 4;
-  const int64_t units = int64_t(p->d.heads) * p->d.head_dim / E;
-  const dim3 grid(unsigned((p->L + kRopeRows - 1) / kRopeRows), unsigned(p->d.batch));
-  const unsigned threads = unsigned(std::min<int64_t>(1024, (units + 63) / 64 * 64));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const float2* cs = reinterpret_cast<const float2*>(p->d_rope);
-  const int32_t lr_w = std::max(p->d.lr_w, 1);
-  if (p->d.dtype == UG_BF16)
-    hipLaunchKernelGGL(permute_rope_kernel<__bf16>, grid, dim3(threads), 0, s, static_cast<const __bf16*>(q_raster),
-                       static_cast<const __bf16*>(k_raster), static_cast<__bf16*>(q_perm),
-                       static_cast<__bf16*>(k_perm), int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w,
-                       p->d.rho, p->d.heads, p->d.head_dim, p->d_perm, p->d_lr_perm, cs);
-  else
-    hipLaunchKernelGGL(permute_rope_kernel<float>, grid, dim3(threads), 0, s, static_cast<const float*>(q_raster),
-                       static_cast<const float*>(k_raster), static_cast<float*>(q_perm), static_cast<float*>(k_perm),
-                       int32_t(p->L), int32_t(p->T), int32_t(p->N), p->d.hr_w, lr_w, p->d.rho, p->d.heads,
-                       p->d.head_dim, p->d_perm, p->d_lr_perm, cs);
-  return launch_status("ug_permute_rope");
+  return permute_rope_common<false>(p, q_raster, k_raster, q_perm, k_perm, stream, "ug_permute_rope");
+}
+
+ug_status ug_permute_rope_bwd(ug_plan_t p, const void* dq_perm, const void* dk_perm, void* dq_raster,
+                              void* dk_raster, void* stream) {
+  return permute_rope_common<true>(p, dq_perm, dk_perm, dq_raster, dk_raster, stream, "ug_permute_rope_bwd");
 }
 
 }  // extern "C"

@@ -236,8 +236,16 @@ ug_status ug_attn_fwd_raster(ug_plan_t plan, const void* q, const void* k, const
  * gradients with respect to the rotated Q, K to gradients with respect to
  * Q, K.  Same arguments and rules as ug_rope2d.
  *
+ * ug_permute_rope_bwd: the transpose of ug_permute_rope, for the gradients:
+ * dq_raster/dk_raster = ug_rope2d_bwd of dq_perm/dk_perm followed by
+ * ug_unpermute, in one read and one write (bit-identical to the two calls).
+ * The inputs are not modified.  Out of place: no output may overlap an
+ * input, and dq_raster must not overlap dk_raster.  Any plan ug_rope2d
+ * accepts.
+ *
  * A layer's backward in raster layout is then: ug_permute(dO) ->
- * ug_attn_bwd -> ug_rope2d_bwd(dq, dk) -> ug_unpermute of dq, dk and dv.
+ * ug_attn_bwd -> ug_permute_rope_bwd(dq, dk) and ug_unpermute(dv) (or,
+ * unfused, ug_rope2d_bwd(dq, dk) -> ug_unpermute of dq, dk and dv).
  */
 ug_status ug_attn_fwd_lse(ug_plan_t plan, const void* q, const void* k, const void* v, void* o, float* lse,
                           void* workspace, void* stream);
@@ -245,6 +253,8 @@ ug_status ug_attn_bwd(ug_plan_t plan, const void* q, const void* k, const void* 
                       const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* workspace,
                       void* stream);
 ug_status ug_rope2d_bwd(ug_plan_t plan, void* dq_perm, void* dk_perm, void* stream);
+ug_status ug_permute_rope_bwd(ug_plan_t plan, const void* dq_perm, const void* dk_perm, void* dq_raster,
+                              void* dk_raster, void* stream);
 
 /*
  * Guidance-weighted warm start (关键设计 4; gist.science summary 2.C): the HR

@@ -188,6 +188,30 @@ def test_fused_entry_points_bit_exact(U, name):
     assert torch.equal(as_bits(o_fused), as_bits(o_sep))
 
 
+@pytest.mark.parametrize("name", ["tiny", "small_ragged", "small_d64", "small_ragged_f32", "1k", "ragged"] + CORR
+                         + ["edge:" + c for c in ("batch2", "no_lr", "no_text", "corr_batch2", "corr_lr_overhang")])
+def test_permute_rope_bwd_bit_exact(U, name):
+    """ug_permute_rope_bwd == ug_rope2d_bwd + ug_unpermute of dq and dk, bit
+    for bit, and leaves its inputs untouched (arbitrary values stand in for
+    the gradients)."""
+    import torch
+    if name.startswith("edge:"):
+        w = WL.WORKLOADS["small_ragged_f32"].with_(dtype="bf16", cfg_id=20, **EDGE[name[5:]])
+    else:
+        w = WL.WORKLOADS[name]
+    p = plan_of(U, w)
+    gq, gk, _ = qkv_device(w)
+    as_bits = (lambda t: t.view(torch.int16)) if w.dtype == "bf16" else (lambda t: t.view(torch.int32))
+    gq0, gk0 = gq.clone(), gk.clone()
+    dq, dk = U.ug_permute_rope_bwd(p, gq, gk)
+    sq, sk = gq.clone(), gk.clone()
+    U.ug_rope2d_bwd(p, sq, sk)
+    rq, rk = U.ug_unpermute(p, sq), U.ug_unpermute(p, sk)
+    torch.cuda.synchronize()
+    assert torch.equal(as_bits(dq), as_bits(rq)) and torch.equal(as_bits(dk), as_bits(rk))
+    assert torch.equal(as_bits(gq), as_bits(gq0)) and torch.equal(as_bits(gk), as_bits(gk0))
+
+
 def test_attention_is_deterministic(U):
     import torch
     w = WL.WORKLOADS["1k"]
@@ -257,5 +281,9 @@ def test_argument_errors_on_device(U):
                                s) == 1
     assert lib.ug_attn_fwd_raster(p.handle, vp(q.data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()), vp(v.data_ptr()),
                                   None, s) == 1
+    assert lib.ug_permute_rope_bwd(p.handle, vp(q.data_ptr()), vp(k.data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()),
+                                   s) == 1
+    assert lib.ug_permute_rope_bwd(p.handle, vp(q.data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()), vp(v.data_ptr()),
+                                   s) == 1
     with pytest.raises(ValueError):
         U.ug_permute(p, q[:, :10].contiguous())
