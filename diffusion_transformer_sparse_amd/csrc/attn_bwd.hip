@@ -89,23 +89,19 @@ struct Loader {
 #pragma unroll
     for (int i = 0; i < L::kLoads; ++i) off[i] = uint32_t(row_of(i, tid) * rs * 2 + lchunk_of(i, tid) * 16);
   }
+  // Rows nv .. 63 of a ragged tile read as zeros (the buffer descriptor
+  // covers the nv valid rows only).  A zero row contributes nothing: a zero
+  // K row to dQ, a zero Q row to dK, a zero dO row to dV (and its dP is 0,
+  // so dS = P * (0 - Delta) only meets zero rows), so no mask is needed.
   __device__ __forceinline__ void issue(const __bf16* src, int64_t rs, int32_t ks, int32_t nv, char* tile, int tid,
                                         int wave) const {
     const char* base = reinterpret_cast<const char*>(src + int64_t(ks) * rs);  // wave-uniform
-    if (nv == kRows) {
+    const int32_t nvs = __builtin_amdgcn_readfirstlane(nv);
+    const int32_t bytes = (nvs > 0 ? nvs : 0) * int32_t(rs) * 2;
 #pragma unroll
-      for (int i = 0; i < L::kLoads; ++i)
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(base + off[i]),
-                                         (lds_void*)(tile + (i * kThreads + wave * 64) * 16), 16, 0, 0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < L::kLoads; ++i) {
-        const int r = min(row_of(i, tid), nv - 1);
-        const char* gp = base + int64_t(r) * rs * 2 + lchunk_of(i, tid) * 16;
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(gp),
-                                         (lds_void*)(tile + (i * kThreads + wave * 64) * 16), 16, 0, 0);
-      }
-    }
+    for (int i = 0; i < L::kLoads; ++i)
+      load_lds<16>(base, off[i], (lds_void*)(tile + (i * kThreads + wave * 64) * 16), bytes);
+    (void)tid;
   }
 };
 
@@ -352,8 +348,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int key = 32 * mb + 8 * (j >> 2) + 4 * g + (j & 3);
-        float pv = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -lse2));
-        if (nv < kRows && key >= nv) pv = 0.f;
+        // P <= 1 for every allowed key; the clamp (free on v_exp) keeps
+        // the zero rows of a ragged tile finite whatever the row's LSE.
+        const float pv = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(fmaf(s[j], c2, -lse2)), 0.f, 1.f);
         dsb[2 * mb + (j >> 3)][j & 7] = __bf16(pv * (dp[j] - dlt));
       }
     }
@@ -466,12 +463,11 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
     const char* qt = smem + slot * TB;
     const char* dot = smem + 2 * TB + slot * TB;
     const float* st = reinterpret_cast<const float*>(smem + 4 * TB + slot * SB);
-    // Query rows at or past `lim` contribute nothing to this lane's key: the
-    // ragged tail of the tile, or all rows when the key does not see the range.
+    // Whether this lane's key sees the tile's query range (corresponding-LR
+    // key tiles); a ragged tail needs no mask (its rows are zero).
     const bool sees = (kmask >> rcur) & 1;
     const uint64_t seen = __ballot(sees);
-    const int32_t lim = sees ? nv : 0;
-    const bool full = nv == kRows && seen == ~uint64_t(0);  // uniform
+    const bool all_see = seen == ~uint64_t(0);  // uniform
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       if (seen == 0) break;  // no key of this wave sees the range (uniform)
@@ -493,8 +489,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int j = 4 * a + e;
-            float pv = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -lv[e]));
-            if (!full && row0 + e >= lim) pv = 0.f;
+            float pv = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(fmaf(s[j], c2, -lv[e])), 0.f, 1.f);
+            if (!all_see && !sees) pv = 0.f;
             pb[4 * a2 + e] = __bf16(pv);
             dsb[4 * a2 + e] = __bf16(pv * (dp[j] - dl[e]));
           }

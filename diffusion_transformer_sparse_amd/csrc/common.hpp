@@ -38,9 +38,8 @@ __device__ __forceinline__ float pair_sum(float x) {
 // vector-memory counter only, whereas it counts the global form as an LDS
 // event of unknown order, after which every LDS wait of the wave becomes a
 // full drain.  The descriptor (raw, stride 0, 32-bit data format) is built
-// from a wave-uniform base, so it lives in scalar registers.  (Measured: 2-3%
-// faster in the forward kernel; the backward kernels schedule worse with it
-// and keep the global form.)
+// from a wave-uniform base, so it lives in scalar registers.  Its bounds
+// check also zero-fills the rows past a ragged tile's end.
 constexpr int kBufferFlags = 0x00020000;
 
 // Lanes whose voffset + size exceeds `bytes` read zeros instead (the buffer
