@@ -163,7 +163,9 @@ def test_attention_backward_matches_oracle(U, name, qscale):
         grad_close(dv[:, h], rv, w, f"{name} x{qscale} dv h{h}")
 
 
-def run_layer_bwd(U, w):
+def run_layer_bwd(U, w, host=True):
+    """TrainLayer forward + backward; the results on the host in fp64, or
+    (host=False) as device tensors."""
     import torch
     p = U.ug_plan(U.desc_of(w))
     q, k, v, do = inputs(w)
@@ -173,6 +175,8 @@ def run_layer_bwd(U, w):
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     layer.backward(do, dq, dk, dv)
     torch.cuda.synchronize()
+    if not host:
+        return p, [out, dq, dk, dv]
     return p, [to_host_f64(x, w.dtype) for x in (out, dq, dk, dv)]
 
 
@@ -229,28 +233,31 @@ def test_backward_is_deterministic(U):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["4k", "4k_corr"])
+@pytest.mark.parametrize("name", ["4k", "4k_corr", "ragged", "8k"])
 def test_full_size_backward_sampled(U, name):
-    """The 256x256 layer's backward at full size; the oracle recomputes dq of
-    sampled query rows (corner, edge, interior HR, text, LR) and dk, dv of
-    sampled HR key rows (with lr_mode 1 also LR key rows) one by one."""
+    """A layer's backward at full size (256x256, the ragged 250x380 grid with
+    batch 2, 512x512); the oracle recomputes dq of sampled query rows
+    (corner, edge, interior HR, text, LR) and dk, dv of sampled HR key rows
+    (with lr_mode 1 also LR key rows) one by one."""
     w = WL.WORKLOADS[name]
-    _, (_, dq, dk, dv) = run_layer_bwd(U, w)
+    _, (_, dq_d, dk_d, dv_d) = run_layer_bwd(U, w, host=False)
     geo = O.geometry_of(w)
-    T, W = w.n_text, w.hr_w
+    T, W, H = w.n_text, w.hr_w, w.hr_h
     qrows = np.array([0, T - 1, T, T + 15 * W + 16, T + 100 * W + 37, T + w.n_hr - 1, T + w.n_hr,
                       w.seq_len - 1])
-    krows = [T + 16 * W + 16, T + 255 * W + 3]
+    krows = [T + 16 * W + 16, T + (H - 1) * W + 3]
     if w.lr_mode == 1:  # an LR key is then seen by nine windows' queries, not all of them
         krows += [T + w.n_hr, T + w.n_hr + 37 * w.lr_w + 5, w.seq_len - 1]
     krows = np.array(krows)
+    rows_of = lambda t, r: to_host_f64(t[0, r.tolist()].contiguous(), w.dtype)  # batch 0, sampled rows only
+    dq, dk, dv = rows_of(dq_d, qrows), rows_of(dk_d, krows), rows_of(dv_d, krows)
     for h in (0, w.heads - 1):
         qh, kh, vh, doh = (WL.head_f64(w, t, h) for t in (WL.Q, WL.K, WL.V, WL.DO))
         rq = O.backward_query_rows(geo, qh, kh, vh, doh, w.rope_theta, qrows)
-        grad_close(dq[0][qrows, h], rq, w, f"{name} dq h{h}", qrows)
+        grad_close(dq[:, h], rq, w, f"{name} dq h{h}", qrows)
         rk, rv = O.backward_key_rows(geo, qh, kh, vh, doh, w.rope_theta, krows)
-        grad_close(dk[0][krows, h], rk, w, f"{name} dk h{h}", krows)
-        grad_close(dv[0][krows, h], rv, w, f"{name} dv h{h}", krows)
+        grad_close(dk[:, h], rk, w, f"{name} dk h{h}", krows)
+        grad_close(dv[:, h], rv, w, f"{name} dv h{h}", krows)
 
 
 def test_backward_argument_errors(U):
