@@ -32,7 +32,7 @@ Sources (cited by page title and section):
 Everything is computed in float64, in RASTER order (text rows, then HR rows
 r*W + c, then LR rows m*w + n), and every mask decision is taken from 2D
 coordinates, never from a permutation.  Readings of points the pages leave
-open (all listed in the design doc's table of readings):
+open (R1-R12, each taken as the plainest reading the rest of the pages supports):
   R1 windows and tokens inside a window are both ordered row-major;
   R2 ragged grids use a ceil partition with partial edge windows and a compact
      permutation (no padding);
