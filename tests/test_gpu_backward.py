@@ -206,6 +206,10 @@ EDGE_BWD = {
     "corr_overhang": dict(lr_mode=1, lr_h=14, lr_w=14),
     "corr_radius2": dict(lr_mode=1, radius=2),
     "corr_window8": dict(lr_mode=1, window=8),
+    # 9x9 windows at radius 4: interior windows see 81 windows, more query
+    # ranges than one key tile may hold, so plain and grouped (masked) LR
+    # key tiles share one dK/dV launch
+    "corr_radius4_plain_and_grouped": dict(lr_mode=1, window=8, radius=4, hr_h=72, hr_w=72, lr_h=18, lr_w=18),
 }
 
 

@@ -79,6 +79,21 @@ def test_corresponding_lr_tables(H, W, l, r, T, lh, lw, rho):
     assert p.info["pairs_per_head"] == O.pair_count(geo) == int(O.allowed_dense(geo).sum())
 
 
+@pytest.mark.parametrize("H,W,l,r,rho", [(160, 160, 16, 4, 4), (96, 80, 8, 4, 2), (160, 160, 16, 3, 4),
+                                         (72, 72, 8, 5, 4)])
+def test_corresponding_lr_key_tiles_at_large_radius(H, W, l, r, rho):
+    """lr_mode 1 key-major view where one window's neighbourhood alone exceeds
+    the 64 query ranges a key tile may hold (interior windows at radius >= 4):
+    those windows get plain key tiles, the rest grouped, masked ones.  The
+    plan checks internally that the masked transpose counts the forward's
+    pairs; the count itself must equal the oracle's."""
+    lh, lw = -(-H // rho), -(-W // rho)
+    d = U.make_desc(H, W, lh, lw, 5, 2, 64, "f32", window=l, radius=r, rho=rho, host_only=True, lr_mode=1)
+    p = U.ug_plan(d)
+    assert p.info["pairs_per_head"] == O.pair_count(O.Geometry(H, W, lh, lw, 5, l, r, rho, lr_mode=1))
+    p.close()
+
+
 @pytest.mark.parametrize("H,W,l,r,T,lh,lw", [(3, 5, 2, 1, 2, 1, 2), (17, 33, 16, 1, 0, 5, 9), (40, 40, 8, 2, 7, 0, 0),
                                               (64, 48, 32, 1, 5, 16, 12), (20, 20, 64, 0, 3, 5, 5),
                                               (33, 65, 16, 0, 0, 9, 17)])
