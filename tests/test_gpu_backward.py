@@ -239,8 +239,8 @@ def test_backward_is_deterministic(U):
 
 @pytest.mark.parametrize("name", ["4k", "4k_corr", "ragged", "8k"])
 def test_full_size_backward_sampled(U, name):
-    """A layer's backward at full size (256x256, the ragged 250x380 grid with
-    batch 2, 512x512); the oracle recomputes dq of sampled query rows
+    """A layer's backward at full size (256x256, the ragged 250x380 grid,
+    512x512); the oracle recomputes dq of sampled query rows
     (corner, edge, interior HR, text, LR) and dk, dv of sampled HR key rows
     (with lr_mode 1 also LR key rows) one by one."""
     w = WL.WORKLOADS[name]
