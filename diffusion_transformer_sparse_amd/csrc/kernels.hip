@@ -316,6 +316,14 @@ __global__ __launch_bounds__(1024) void permute_rope_kernel(const T* __restrict_
 // the PV product and the row sum taken over the same rounded P; fp32:
 // v_mfma_f32_32x32x2_f32.  The output goes through LDS so every row is
 // written with full 16-byte stores.
+// Persistent grid: one workgroup per CU takes query tiles from the plan's
+// eight per-XCD queues (the workgroup order, XCD x's queue at items x,
+// x + 8, ...) through an atomic cursor per queue, its own XCD's queue first,
+// then the others'.  The XCDs run at different speeds (up to 4% per tile on
+// the same work) and the hardware dispatches workgroups to them in lockstep,
+// so a static one-tile-per-workgroup grid leaves CUs idle between tiles and
+// at the end; taking tiles dynamically keeps every CU busy until the queues
+// are empty.
 // ---------------------------------------------------------------------------
 constexpr int kAttnThreads = 512;
 constexpr int kAttnWaves = kAttnThreads / 64;
@@ -339,6 +347,8 @@ struct AttnParams {
   const int32_t* out_lr_perm;  // non-null (with out_perm): LR row T+N+i to T+N+out_lr_perm[i]
   float* lse;                  // non-null: natural-log LSE of each row, [batch*heads][lse_rows]
   int64_t lse_rows;
+  int32_t* queue;     // this launch's cursor slot: 8 per-XCD queue cursors, then the finished-workgroup count
+  int32_t queue_len;  // items per XCD queue (blocks / 8)
 };
 
 
@@ -428,39 +438,54 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const char* ktile, const
   }
 }
 
+// Kernel arguments through an opaque pointer: each value is loaded where it is
+// used, once per query tile, instead of being hoisted out of the item loop and
+// held in scalar registers across the tile loop.
+typedef __attribute__((address_space(4))) const AttnParams* KArgs;
+__device__ __forceinline__ KArgs kernel_args() {
+  KArgs x = (KArgs)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
+// One query tile (plan item `item`) of the attention.
 template <typename T, int D>
-__global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
+__device__ __forceinline__ void attn_item(KArgs kp, int32_t item, char* smem, ug::Range* s_rng) {
   using Lds = AttnLds<T, D>;
   constexpr bool kBF = Lds::kBF;
   constexpr int TB = Lds::kTileBytes;
-  __shared__ __attribute__((aligned(1024))) char smem[Lds::kTotalBytes];
   // K ring at [0, 2*TB), V ring at [2*TB, 4*TB)
 
-  const ug::Block blk = p.blocks[blockIdx.x];
-  if (blk.task < 0) return;  // idle workgroup (uniform)
-  const ug::Task task = p.tasks[blk.task];
-  const int32_t b = blk.bh / p.heads, h = blk.bh - b * p.heads;
-  const int64_t hoff = int64_t(b) * p.batch_stride + int64_t(h) * D;
-  const T* __restrict__ qg = static_cast<const T*>(p.q) + hoff;
-  const T* __restrict__ kg = static_cast<const T*>(p.k) + hoff;
-  const T* __restrict__ vg = static_cast<const T*>(p.v) + hoff;
-  T* __restrict__ og = static_cast<T*>(p.o) + hoff;
-  const int64_t rs = p.row_stride;
+  const ug::Block blk = kp->blocks[item];
+  const ug::Task task = kp->tasks[blk.task];
+  const int32_t b = blk.bh / kp->heads, h = blk.bh - b * kp->heads;
+  const int64_t hoff = int64_t(b) * kp->batch_stride + int64_t(h) * D;
+  const T* __restrict__ qg = static_cast<const T*>(kp->q) + hoff;
+  const T* __restrict__ kg = static_cast<const T*>(kp->k) + hoff;
+  const T* __restrict__ vg = static_cast<const T*>(kp->v) + hoff;
+  T* __restrict__ og = static_cast<T*>(kp->o) + hoff;
+  const int64_t rs = kp->row_stride;
 
-  const int tid = threadIdx.x;
+  // The thread index is made opaque so that nothing derived from it is
+  // hoisted out of the item loop (values kept live across the tile loop would
+  // make the compiler fall back to a serial LDS-read schedule); the mask
+  // gives its range back to alias analysis, which proves that the tile loads
+  // in flight do not overlap the ring slot being read.
+  int tid_ = int(threadIdx.x);
+  asm volatile("" : "+v"(tid_));
+  const int tid = tid_ & (kAttnThreads - 1);
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int32_t qrow = task.q0 + wave * 32 + l32;
   const int32_t qload = qrow < task.q1 ? qrow : task.q1 - 1;
-  const float c2 = p.scale_log2;
+  const float c2 = kp->scale_log2;
 
   // The task's key ranges (at most ug::kAttnMaxRanges, checked at launch)
-  // are staged in LDS, so moving to the next range inside the tile loop is an
-  // LDS read rather than a global load that would wait on the tile loads in
-  // flight.
-  __shared__ ug::Range s_rng[ug::kAttnMaxRanges];
+  // are staged in LDS (s_rng), so moving to the next range inside the tile
+  // loop is an LDS read rather than a global load that would wait on the tile
+  // loads in flight.
   const int32_t nr = task.r1 - task.r0;
-  if (tid < nr) s_rng[tid] = p.ranges[task.r0 + tid];
+  if (tid < nr) s_rng[tid] = kp->ranges[task.r0 + tid];
 
   // The wave's queries as the B operand of S^T = K Q^T.
   constexpr int kQRegs = kBF ? D / 16 : D / 2;
@@ -681,10 +706,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
 
   // ---- epilogue: combine the lane halves' row sums, normalise, and write
   // the wave's 32 x D output block through LDS (swizzled rows) as full rows.
+  kp = kernel_args();  // the epilogue's arguments are loaded here, not kept across the loop
   const float total = pair_sum(lsum);
   const float inv = 1.0f / total;
-  if (p.lse && g == 0 && qrow < task.q1)  // log(sum_j exp(s_j)) = (m2 + log2(total)) * ln 2
-    p.lse[int64_t(blk.bh) * p.lse_rows + qrow] = (m2 + __log2f(total)) * 0.6931471805599453f;
+  if (kp->lse && g == 0 && qrow < task.q1)  // log(sum_j exp(s_j)) = (m2 + log2(total)) * ln 2
+    kp->lse[int64_t(blk.bh) * kp->lse_rows + qrow] = (m2 + __log2f(total)) * 0.6931471805599453f;
   char* const ost = smem + wave * 32 * RB;
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
@@ -710,16 +736,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
   // are clamped for the lookup and skipped at the store), so that all the
   // lookups are in flight together.
   int32_t orow[kPasses];
-  if (p.out_perm) {  // uniform
+  if (kp->out_perm) {  // uniform
 #pragma unroll
     for (int pass = 0; pass < kPasses; ++pass) {
       const int32_t row = min(task.q0 + wave * 32 + pass * rows_per_pass + lane / Lds::kChunks, task.q1 - 1);
-      const bool hr = row >= p.T && row < p.T + p.N;
-      const bool lr = row >= p.T + p.N && p.out_lr_perm != nullptr;
-      const int32_t* tab = lr ? p.out_lr_perm : p.out_perm;
-      const int32_t idx = hr ? row - p.T : lr ? row - p.T - p.N : 0;
+      const bool hr = row >= kp->T && row < kp->T + kp->N;
+      const bool lr = row >= kp->T + kp->N && kp->out_lr_perm != nullptr;
+      const int32_t* tab = lr ? kp->out_lr_perm : kp->out_perm;
+      const int32_t idx = hr ? row - kp->T : lr ? row - kp->T - kp->N : 0;
       const int32_t v = tab[idx];
-      orow[pass] = hr ? p.T + v : lr ? p.T + p.N + v : row;
+      orow[pass] = hr ? kp->T + v : lr ? kp->T + kp->N + v : row;
     }
   } else {
 #pragma unroll
@@ -733,6 +759,48 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
     const uint4 val = *reinterpret_cast<const uint4*>(ost + r * RB + ((cc ^ Lds::k_swz(r)) * 16));
     if (task.q0 + wave * 32 + r < task.q1)
       *reinterpret_cast<uint4*>(og + int64_t(orow[pass]) * rs + cc * Lds::kEl16) = val;
+  }
+}
+
+
+// Next item for a workgroup on XCD x0: its own queue first, then the other
+// XCDs' queues; -1 when all are empty.  A cursor past the end of its queue, or
+// on an idle entry that pads a short queue, means that queue is empty.
+__device__ __forceinline__ int32_t attn_grab(KArgs kp, int32_t x0) {
+  for (int32_t k = 0; k < ug::kXcds; ++k) {
+    const int32_t x = (x0 + k) & (ug::kXcds - 1);
+    const int32_t c = __hip_atomic_fetch_add(kp->queue + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c < kp->queue_len && kp->blocks[c * ug::kXcds + x].task >= 0) return c * ug::kXcds + x;
+  }
+  return -1;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
+  (void)p;  // read through kernel_args()
+  using Lds = AttnLds<T, D>;
+  __shared__ __attribute__((aligned(1024))) char smem[Lds::kTotalBytes];
+  __shared__ ug::Range s_rng[ug::kAttnMaxRanges];
+  __shared__ int32_t s_item;
+  for (;;) {
+    if (threadIdx.x == 0) {
+      const int32_t xcc = int32_t(__builtin_amdgcn_s_getreg((31 << 11) | 20));  // HW_REG_XCC_ID
+      s_item = attn_grab(kernel_args(), xcc & (ug::kXcds - 1));
+    }
+    __syncthreads();
+    const int32_t item = s_item;
+    if (item < 0) break;
+    attn_item<T, D>(kernel_args(), item, smem, s_rng);
+    __syncthreads();  // the next item reuses the LDS and s_item
+  }
+  // The last workgroup to finish clears the cursor slot for a later launch:
+  // every other workgroup has made its last (failed) grab before counting
+  // itself finished.
+  if (threadIdx.x == 0) {
+    KArgs kp = kernel_args();
+    if (__hip_atomic_fetch_add(kp->queue + ug::kXcds, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        int32_t(gridDim.x) - 1)
+      for (int x = 0; x <= ug::kXcds; ++x) __hip_atomic_store(kp->queue + x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -759,7 +827,8 @@ ug_status gather(ug_plan_t p, const void* src, void* dst, const int32_t* table, 
 
 template <typename T, int D>
 void launch_attn(ug_plan_t p, const AttnParams& ap, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3(unsigned(p->blocks.size())), dim3(kAttnThreads), 0, s, ap);
+  const unsigned grid = unsigned(std::min<size_t>(size_t(p->cus), p->blocks.size()));
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3(grid), dim3(kAttnThreads), 0, s, ap);
 }
 
 ug_status attn_common(ug_plan_t p, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -807,6 +876,8 @@ ug_status attn_common(ug_plan_t p, const void* q, const void* k, const void* v, 
   ap.out_lr_perm = raster_out ? p->d_lr_perm : nullptr;
   ap.lse = lse;
   ap.lse_rows = p->L;
+  ap.queue = p->next_queue_slot();
+  ap.queue_len = int32_t(p->blocks.size() / ug::kXcds);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = p->d.dtype == UG_BF16;
   if (bf && p->d.head_dim == 128)

@@ -359,14 +359,16 @@ void build_key_tasks(ug_plan_s& p) {
   if (pairs != p.pairs) throw std::logic_error("transposed mask pair count differs from the forward's");
 }
 
-// Workgroup order.  Hardware hands workgroup i to XCD i % 8, and each XCD has
-// its own L2, so the order is built per XCD: every XCD gets a queue whose
-// long items (query tiles with many more key tiles than the average, i.e.
-// text rows) come first, longest first, then a contiguous slice of the
-// remaining items in (batch, head, tile) order, so that tiles of one head
-// that share neighbour windows and the LR keys run on the same L2.  Queues
-// are balanced by key-tile count and interleaved; short queues are padded
-// with idle workgroups.
+// Per-XCD work queues.  Each XCD has its own L2, so the order is built per
+// XCD: every XCD gets a queue whose long items (query tiles with many more
+// key tiles than the average, i.e. text rows) come first, longest first, then
+// a contiguous slice of the remaining items in (batch, head, tile) order, so
+// that tiles of one head that share neighbour windows and the LR keys run on
+// the same L2.  Queues are balanced by key-tile count and interleaved (item
+// k * 8 + x is the k-th of XCD x's queue); short queues are padded with idle
+// items.  The attention forward's persistent workgroups take items from these
+// queues dynamically; the backward launches one workgroup per item, which the
+// hardware hands to XCD i % 8 in the same interleaved order.
 std::vector<ug::Block> order_blocks(const std::vector<ug::Task>& tasks, const std::vector<ug::Range>& ranges,
                                     int64_t BH) {
   const int X = ug::kXcds;
@@ -433,7 +435,7 @@ ug_status upload(const std::vector<T>& h, T** d) {
 void free_device(ug_plan_s* p) {
   void* ptrs[] = {p->d_perm,    p->d_inv,     p->d_lr_perm, p->d_lr_inv,     p->d_rope,
                   p->d_tasks,   p->d_ranges,  p->d_blocks,  p->d_ktasks,     p->d_kranges,
-                  p->d_kblocks, p->d_kmasks, p->d_kmask_off};
+                  p->d_kblocks, p->d_kmasks, p->d_kmask_off, p->d_queue};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
   p->d_perm = p->d_inv = nullptr;
@@ -447,6 +449,7 @@ void free_device(ug_plan_s* p) {
   p->d_kblocks = nullptr;
   p->d_kmasks = nullptr;
   p->d_kmask_off = nullptr;
+  p->d_queue = nullptr;
 }
 
 ug_status check_device(ug_plan_s* p) {
@@ -463,6 +466,22 @@ ug_status check_device(ug_plan_s* p) {
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(UG_ERR_UNSUPPORTED, std::string("ug_plan: kernels are built for gfx950, device is ") + prop.gcnArchName);
   p->device = dev;
+  p->cus = prop.multiProcessorCount;
+  if (p->cus <= 0) return fail(UG_ERR_HIP, "ug_plan: the device reports no compute units");
+  return UG_OK;
+}
+
+// Zeroed work-queue cursor slots of the persistent attention grid.
+ug_status alloc_queue(ug_plan_s* p) {
+  const size_t bytes = size_t(kQueueSlots) * kQueueSlotInts * sizeof(int32_t);
+  if (hipMalloc(reinterpret_cast<void**>(&p->d_queue), bytes) != hipSuccess) {
+    p->d_queue = nullptr;
+    (void)hipGetLastError();
+    return fail(UG_ERR_OUT_OF_MEMORY, "ug_plan: hipMalloc of the work-queue cursors failed");
+  }
+  if (hipMemset(p->d_queue, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+    return fail(UG_ERR_HIP, std::string("ug_plan: clearing the work-queue cursors failed: ") +
+                                hipGetErrorString(hipGetLastError()));
   return UG_OK;
 }
 
@@ -517,6 +536,7 @@ ug_status ug_plan(const ug_desc* desc, ug_plan_t* out) {
     if (s == UG_OK) s = ug::upload(p->kblocks, &p->d_kblocks);
     if (s == UG_OK) s = ug::upload(p->kmask_off, &p->d_kmask_off);
     if (s == UG_OK) s = ug::upload(p->kmasks, &p->d_kmasks);
+    if (s == UG_OK) s = ug::alloc_queue(p);
     if (s != UG_OK) {
       ug::free_device(p);
       delete p;

@@ -2,6 +2,7 @@
 // kernel launchers (kernels.hip).  Not part of the public ABI.
 #pragma once
 
+#include <atomic>
 #include <cstdint>
 #include <string>
 #include <vector>
@@ -31,6 +32,12 @@ constexpr int kAttnQueryTile = 256;  // query rows per workgroup (8 waves x 32)
 constexpr int kAttnKeyTile = 64;     // key rows per LDS stage
 constexpr int kXcds = 8;             // gfx950: workgroups round-robin over 8 XCDs
 constexpr int kAttnMaxRanges = 64;   // key ranges one query tile may have (staged in LDS)
+// Work-queue cursors of the persistent attention grid: each launch takes one
+// slot of kQueueSlotInts int32 (one cursor per XCD queue, then the count of
+// workgroups that have finished), round-robin over kQueueSlots slots, so that
+// launches with one plan that run at the same time use different cursors.
+constexpr int kQueueSlots = 64;
+constexpr int kQueueSlotInts = 16;
 
 }  // namespace ug
 
@@ -88,6 +95,15 @@ struct ug_plan_s {
   ug::Block* d_kblocks = nullptr;
   int32_t* d_kmask_off = nullptr;
   uint64_t* d_kmasks = nullptr;  // null when no key tile is masked
+
+  // Persistent attention grid: one workgroup per compute unit, and the
+  // zeroed work-queue cursor slots (each launch leaves its slot at zero).
+  int32_t cus = 0;
+  int32_t* d_queue = nullptr;
+  std::atomic<uint32_t> launches{0};
+  int32_t* next_queue_slot() {
+    return d_queue + size_t(launches.fetch_add(1, std::memory_order_relaxed) % ug::kQueueSlots) * ug::kQueueSlotInts;
+  }
 };
 
 namespace ug {

@@ -28,7 +28,12 @@
  *    device tables.  No entry point allocates device memory except ug_plan.
  *  - Launches are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  Device faults surface at the caller's next synchronisation.
- *    A plan is immutable after creation and may serve several streams at once.
+ *    A plan's tables are immutable after creation and a plan may serve
+ *    several streams at once.  The attention forward runs as a persistent
+ *    grid whose workgroups take query tiles from work queues through atomic
+ *    cursors that the plan owns: each launch takes the next of 64 cursor
+ *    slots and leaves it cleared when it ends, so at most 64 attention
+ *    forward launches of one plan may be in flight at the same time.
  */
 #ifndef ULTRAGEN_H
 #define ULTRAGEN_H
@@ -107,7 +112,9 @@ typedef struct ug_info {
   double eff_flops;            /* 4 * D * pairs_per_head * heads * batch */
   int64_t workspace_bytes;     /* bytes ug_attn_fwd needs as workspace (0 today) */
   int64_t attn_tasks;          /* query tiles per (batch, head) */
-  int64_t attn_blocks;         /* workgroups one ug_attn_fwd launches */
+  int64_t attn_blocks;         /* items of the attention's 8 per-XCD work queues (one per query
+                                  tile and batch*head, plus idle padding); ug_attn_fwd launches
+                                  min(compute units, attn_blocks) persistent workgroups */
   int64_t attn_key_tiles;      /* 64-key tiles processed per (batch, head) */
   int64_t rope_positions;      /* rows of the RoPE cos/sin table */
   int64_t bwd_workspace_bytes; /* bytes ug_attn_bwd needs as workspace */
@@ -122,7 +129,8 @@ typedef struct ug_plan_s* ug_plan_t;
  * and inverse, window offsets, window neighbourhoods, the per-query-tile key
  * range list and workgroup order, RoPE cos/sin table computed in double and
  * stored as float) and, unless UG_PLAN_HOST_ONLY, upload them to the current
- * HIP device (synchronous).  The window-first order is 关键设计 1's regrouping
+ * HIP device and allocate the attention's zeroed work-queue cursors (4 KiB)
+ * there (synchronous).  The window-first order is 关键设计 1's regrouping
  * of tokens window by window; the neighbourhood is its adjacent-window
  * interaction.  On success *out owns everything; free it with ug_plan_free
  * once no launched work still uses it.

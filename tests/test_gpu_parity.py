@@ -223,6 +223,35 @@ def test_attention_is_deterministic(U):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+def test_attention_queue_cursors_reused_and_concurrent(U):
+    """The persistent attention grid takes query tiles through per-XCD queue
+    cursors; each launch takes one of the plan's 64 cursor slots and leaves it
+    cleared.  More launches than slots give bit-identical outputs, and
+    launches with one plan on two streams at once match the serial result."""
+    import torch
+    w = WL.WORKLOADS["1k"]
+    p = plan_of(U, w)
+    q, k, v = qkv_device(w)
+    ref = U.ug_attn_fwd(p, q, k, v)
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16)
+    o = torch.empty_like(ref)
+    for i in range(140):  # every slot used at least twice
+        U.ug_attn_fwd(p, q, k, v, o)
+        if i % 20 == 0 or i == 139:
+            torch.cuda.synchronize()
+            assert torch.equal(bits(o), bits(ref)), f"launch {i}"
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = [torch.empty_like(ref) for _ in range(8)]
+    torch.cuda.synchronize()
+    for j, out in enumerate(outs):
+        with torch.cuda.stream(s1 if j % 2 == 0 else s2):
+            U.ug_attn_fwd(p, q, k, v, out)
+    torch.cuda.synchronize()
+    for j, out in enumerate(outs):
+        assert torch.equal(bits(out), bits(ref)), f"concurrent launch {j}"
+
+
 # ------------------------------------------------------------------ edge cases
 
 EDGE = {
