@@ -264,7 +264,36 @@ struct BwdParams {
   const uint64_t* masks;    // bit r: the key row sees the tile's query range r
   float scale_log2;  // log2(e) / sqrt(D)
   float scale;       // 1 / sqrt(D)
+  int32_t* queue;     // this launch's cursor slot: 8 per-XCD queue cursors, then the finished-workgroup count
+  int32_t queue_len;  // items per XCD queue (blocks / 8)
 };
+typedef __attribute__((address_space(4))) const BwdParams* BArgs;
+__device__ __forceinline__ BArgs bwd_args() { return opaque_args<BwdParams>(); }
+
+// Persistent grid of the dQ pass: one workgroup per CU takes query tiles from
+// the plan's per-XCD queues until they are empty, as the attention forward
+// does.  The dK/dV pass keeps one workgroup per key tile: inside an item loop
+// the addresses of its two LDS rings no longer fold into one base plus
+// immediate offsets (twice the address arithmetic per step), which cost more
+// than the dynamic schedule gained.
+template <int kSmem, typename Item>
+__device__ __forceinline__ void run_queue(Item item_fn) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+  __shared__ ug::Range s_rng[ug::kAttnMaxRanges];
+  __shared__ int32_t s_item;
+  for (;;) {
+    if (threadIdx.x == 0) {
+      BArgs kp = bwd_args();
+      s_item = queue_grab(kp->queue, kp->queue_len, kp->blocks, xcc_id());
+    }
+    __syncthreads();
+    const int32_t item = s_item;
+    if (item < 0) break;
+    item_fn(bwd_args(), item, smem, s_rng);
+    __syncthreads();  // the next item reuses the LDS and s_item
+  }
+  if (threadIdx.x == 0) queue_finish(bwd_args()->queue);
+}
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per query tile (the forward's tasks), 8 waves x 32
@@ -275,43 +304,42 @@ struct BwdParams {
 //   dQ^T += K^T dS^T (A: K transposed from LDS, B: dS^T from registers)
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void dq_item(BArgs kp, int32_t item, char* smem, ug::Range* s_rng) {
   using L = Tile<D>;
   constexpr int TB = L::kBytes;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];  // K ring [0, 2TB), V ring [2TB, 4TB)
-  __shared__ ug::Range s_rng[ug::kAttnMaxRanges];
 
-  const ug::Block blk = p.blocks[blockIdx.x];
-  if (blk.task < 0) return;  // idle workgroup (uniform)
-  const ug::Task task = p.tasks[blk.task];
-  const int32_t b = blk.bh / p.heads, h = blk.bh - b * p.heads;
-  const int64_t hoff = int64_t(b) * p.batch_stride + int64_t(h) * D;
-  const int64_t rs = p.row_stride;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const ug::Block blk = kp->blocks[item];
+  const ug::Task task = kp->tasks[blk.task];
+  const int32_t b = blk.bh / kp->heads, h = blk.bh - b * kp->heads;
+  const int64_t hoff = int64_t(b) * kp->batch_stride + int64_t(h) * D;
+  const int64_t rs = kp->row_stride;
+  // wave index in a scalar register, masked so that alias analysis keeps its range
+  const int tid = opaque_tid<kThreads>(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (kThreads / 64 - 1);
   const int l32 = lane & 31, g = lane >> 5;
   const int32_t qrow = task.q0 + wave * 32 + l32;
   const int32_t qload = min(qrow, task.q1 - 1);
 
   const int32_t nr = task.r1 - task.r0;
-  if (tid < nr) s_rng[tid] = p.ranges[task.r0 + tid];
+  if (tid < nr) s_rng[tid] = kp->ranges[task.r0 + tid];
 
   bf16x8 qf[D / 16], df[D / 16];
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) {
-    qf[i] = *reinterpret_cast<const bf16x8*>(p.q + hoff + qload * rs + 16 * i + 8 * g);
-    df[i] = *reinterpret_cast<const bf16x8*>(p.d_o + hoff + qload * rs + 16 * i + 8 * g);
+    qf[i] = *reinterpret_cast<const bf16x8*>(kp->q + hoff + qload * rs + 16 * i + 8 * g);
+    df[i] = *reinterpret_cast<const bf16x8*>(kp->d_o + hoff + qload * rs + 16 * i + 8 * g);
   }
-  const int64_t srow = int64_t(blk.bh) * p.Lp + qload;
-  const float lse2 = p.lse2[srow];
-  const float dlt = p.delta[srow];
-  const float c2 = p.scale_log2;
+  const int64_t srow = int64_t(blk.bh) * kp->Lp + qload;
+  const float lse2 = kp->lse2[srow];
+  const float dlt = kp->delta[srow];
+  const float c2 = kp->scale_log2;
   __syncthreads();  // s_rng is filled
 
   int32_t ntiles = 0;
   for (int32_t r = 0; r < nr; ++r) ntiles += (s_rng[r].k1 - s_rng[r].k0 + kRows - 1) / kRows;
 
-  const __bf16* kg = p.k + hoff;
-  const __bf16* vg = p.v + hoff;
+  const __bf16* kg = kp->k + hoff;
+  const __bf16* vg = kp->v + hoff;
   Loader<D> ld;
   ld.init(rs, tid);
   LaneOffsets<D> lo;
@@ -363,7 +391,16 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of the next tile have landed
     __syncthreads();
   }
-  store_block<D>(acc, p.scale, smem + wave * 32 * L::RB, p.dq + hoff, rs, task.q0 + wave * 32, task.q1, lane);
+  kp = bwd_args();  // the epilogue's arguments are loaded here, not kept across the loop
+  store_block<D>(acc, kp->scale, smem + wave * 32 * L::RB, kp->dq + hoff, rs, task.q0 + wave * 32, task.q1, lane);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdParams p) {
+  (void)p;  // read through bwd_args()
+  run_queue<4 * Tile<D>::kBytes>([](BArgs kp, int32_t item, char* smem, ug::Range* s_rng) {  // K ring, V ring
+    dq_item<D>(kp, item, smem, s_rng);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -526,8 +563,12 @@ void launch_bwd(ug_plan_t p, BwdParams bp, const __bf16* o, const float* lse, fl
   bp.tasks = p->d_tasks;
   bp.ranges = p->d_ranges;
   bp.blocks = p->d_blocks;
-  if (!p->blocks.empty())
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3(unsigned(p->blocks.size())), dim3(kThreads), 0, s, bp);
+  if (!p->blocks.empty()) {
+    bp.queue = p->next_queue_slot();
+    bp.queue_len = int32_t(p->blocks.size() / ug::kXcds);
+    const unsigned grid = unsigned(std::min<size_t>(size_t(p->cus), p->blocks.size()));
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3(grid), dim3(kThreads), 0, s, bp);
+  }
   bp.tasks = p->d_ktasks;
   bp.ranges = p->d_kranges;
   bp.blocks = p->d_kblocks;

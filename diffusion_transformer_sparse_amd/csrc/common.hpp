@@ -82,6 +82,56 @@ struct TileCursor {
   }
 };
 
+// Item loops of persistent kernels.  Kernel arguments read through an opaque
+// pointer are loaded where they are used, once per item, instead of being
+// hoisted out of the item loop and held in scalar registers across the tile
+// loop.  The thread index is made opaque for the same reason (values derived
+// from it and kept live across the tile loop make the compiler fall back to a
+// serial LDS-read schedule); the mask gives its range back to alias analysis,
+// which proves that tile loads in flight do not overlap the LDS being read.
+template <typename P>
+__device__ __forceinline__ __attribute__((address_space(4))) const P* opaque_args() {
+  auto x = (__attribute__((address_space(4))) const P*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(x));
+  return x;
+}
+template <int kThreads>
+__device__ __forceinline__ int opaque_tid() {
+  static_assert((kThreads & (kThreads - 1)) == 0, "power-of-two workgroup");
+  int t = int(threadIdx.x);
+  asm volatile("" : "+v"(t));
+  return t & (kThreads - 1);
+}
+
+// Work queues of a persistent grid (one workgroup per CU).  The plan lays out
+// eight per-XCD queues interleaved in one item array: item k * 8 + x is the
+// k-th of XCD x's queue, and items with task < 0 pad the short queues.  A
+// launch owns one cursor slot: queue[x] is the cursor of XCD x's queue,
+// queue[8] the number of workgroups that have finished.  The cursors are
+// agent-scope atomics, shared by the XCDs.
+__device__ __forceinline__ int32_t xcc_id() {
+  return int32_t(__builtin_amdgcn_s_getreg((31 << 11) | 20)) & (ug::kXcds - 1);  // HW_REG_XCC_ID
+}
+// Next item for a workgroup on XCD x0: its own XCD's queue first, then the
+// others'; -1 when every queue is empty.  A cursor past the end of its queue
+// or on a padding item means that queue is empty.
+__device__ __forceinline__ int32_t queue_grab(int32_t* queue, int32_t queue_len, const ug::Block* items, int32_t x0) {
+  for (int32_t k = 0; k < ug::kXcds; ++k) {
+    const int32_t x = (x0 + k) & (ug::kXcds - 1);
+    const int32_t c = __hip_atomic_fetch_add(queue + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c < queue_len && items[c * ug::kXcds + x].task >= 0) return c * ug::kXcds + x;
+  }
+  return -1;
+}
+// Once per workgroup, after its last (failed) grab: the last workgroup to
+// finish clears the slot for a later launch.  Every other workgroup has made
+// its last grab before counting itself finished, so no cursor moves after.
+__device__ __forceinline__ void queue_finish(int32_t* queue) {
+  if (__hip_atomic_fetch_add(queue + ug::kXcds, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      int32_t(gridDim.x * gridDim.y * gridDim.z) - 1)
+    for (int x = 0; x <= ug::kXcds; ++x) __hip_atomic_store(queue + x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace dev
 
 namespace host {

@@ -438,15 +438,8 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const char* ktile, const
   }
 }
 
-// Kernel arguments through an opaque pointer: each value is loaded where it is
-// used, once per query tile, instead of being hoisted out of the item loop and
-// held in scalar registers across the tile loop.
 typedef __attribute__((address_space(4))) const AttnParams* KArgs;
-__device__ __forceinline__ KArgs kernel_args() {
-  KArgs x = (KArgs)__builtin_amdgcn_kernarg_segment_ptr();
-  asm volatile("" : "+s"(x));
-  return x;
-}
+__device__ __forceinline__ KArgs kernel_args() { return opaque_args<AttnParams>(); }
 
 // One query tile (plan item `item`) of the attention.
 template <typename T, int D>
@@ -466,15 +459,10 @@ __device__ __forceinline__ void attn_item(KArgs kp, int32_t item, char* smem, ug
   T* __restrict__ og = static_cast<T*>(kp->o) + hoff;
   const int64_t rs = kp->row_stride;
 
-  // The thread index is made opaque so that nothing derived from it is
-  // hoisted out of the item loop (values kept live across the tile loop would
-  // make the compiler fall back to a serial LDS-read schedule); the mask
-  // gives its range back to alias analysis, which proves that the tile loads
-  // in flight do not overlap the ring slot being read.
-  int tid_ = int(threadIdx.x);
-  asm volatile("" : "+v"(tid_));
-  const int tid = tid_ & (kAttnThreads - 1);
-  const int lane = tid & 63, wave = tid >> 6;
+  const int tid = opaque_tid<kAttnThreads>();
+  // wave index in a scalar register (the opaque tid hides that it is uniform),
+  // masked so that alias analysis keeps its range
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (kAttnWaves - 1);
   const int l32 = lane & 31, g = lane >> 5;
   const int32_t qrow = task.q0 + wave * 32 + l32;
   const int32_t qload = qrow < task.q1 ? qrow : task.q1 - 1;
@@ -763,18 +751,6 @@ __device__ __forceinline__ void attn_item(KArgs kp, int32_t item, char* smem, ug
 }
 
 
-// Next item for a workgroup on XCD x0: its own queue first, then the other
-// XCDs' queues; -1 when all are empty.  A cursor past the end of its queue, or
-// on an idle entry that pads a short queue, means that queue is empty.
-__device__ __forceinline__ int32_t attn_grab(KArgs kp, int32_t x0) {
-  for (int32_t k = 0; k < ug::kXcds; ++k) {
-    const int32_t x = (x0 + k) & (ug::kXcds - 1);
-    const int32_t c = __hip_atomic_fetch_add(kp->queue + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (c < kp->queue_len && kp->blocks[c * ug::kXcds + x].task >= 0) return c * ug::kXcds + x;
-  }
-  return -1;
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
   (void)p;  // read through kernel_args()
@@ -784,8 +760,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
   __shared__ int32_t s_item;
   for (;;) {
     if (threadIdx.x == 0) {
-      const int32_t xcc = int32_t(__builtin_amdgcn_s_getreg((31 << 11) | 20));  // HW_REG_XCC_ID
-      s_item = attn_grab(kernel_args(), xcc & (ug::kXcds - 1));
+      KArgs kp = kernel_args();
+      s_item = queue_grab(kp->queue, kp->queue_len, kp->blocks, xcc_id());
     }
     __syncthreads();
     const int32_t item = s_item;
@@ -793,15 +769,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
     attn_item<T, D>(kernel_args(), item, smem, s_rng);
     __syncthreads();  // the next item reuses the LDS and s_item
   }
-  // The last workgroup to finish clears the cursor slot for a later launch:
-  // every other workgroup has made its last (failed) grab before counting
-  // itself finished.
-  if (threadIdx.x == 0) {
-    KArgs kp = kernel_args();
-    if (__hip_atomic_fetch_add(kp->queue + ug::kXcds, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-        int32_t(gridDim.x) - 1)
-      for (int x = 0; x <= ug::kXcds; ++x) __hip_atomic_store(kp->queue + x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (threadIdx.x == 0) queue_finish(kernel_args()->queue);
 }
 
 
