@@ -29,11 +29,12 @@
  *  - Launches are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  Device faults surface at the caller's next synchronisation.
  *    A plan's tables are immutable after creation and a plan may serve
- *    several streams at once.  The attention forward runs as a persistent
- *    grid whose workgroups take query tiles from work queues through atomic
- *    cursors that the plan owns: each launch takes the next of 64 cursor
- *    slots and leaves it cleared when it ends, so at most 64 attention
- *    forward launches of one plan may be in flight at the same time.
+ *    several streams at once.  The attention forward and the dQ pass of
+ *    ug_attn_bwd run as persistent grids whose workgroups take query tiles
+ *    from work queues through atomic cursors that the plan owns: each such
+ *    launch takes the next of 64 cursor slots and leaves it cleared when it
+ *    ends, so at most 64 of them (ug_attn_bwd counts one) may be in flight
+ *    with one plan at the same time.
  */
 #ifndef ULTRAGEN_H
 #define ULTRAGEN_H
