@@ -89,6 +89,8 @@ struct TileCursor {
 // from it and kept live across the tile loop make the compiler fall back to a
 // serial LDS-read schedule); the mask gives its range back to alias analysis,
 // which proves that tile loads in flight do not overlap the LDS being read.
+// P must be the kernel's only explicit argument, taken by value: the AMDGPU
+// ABI places the explicit arguments at the start of the argument segment.
 template <typename P>
 __device__ __forceinline__ __attribute__((address_space(4))) const P* opaque_args() {
   auto x = (__attribute__((address_space(4))) const P*)__builtin_amdgcn_kernarg_segment_ptr();

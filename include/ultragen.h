@@ -34,7 +34,8 @@
  *    from work queues through atomic cursors that the plan owns: each such
  *    launch takes the next of 64 cursor slots and leaves it cleared when it
  *    ends, so at most 64 of them (ug_attn_bwd counts one) may be in flight
- *    with one plan at the same time.
+ *    with one plan at the same time.  A launch captured in a HIP graph keeps
+ *    its slot: replays of that graph must not overlap one another.
  */
 #ifndef ULTRAGEN_H
 #define ULTRAGEN_H
