@@ -6,5 +6,5 @@ from ._binding import (  # noqa: F401
     EXPORTED, LIB_PATH, UG_BF16, UG_F32, UG_PLAN_HOST_ONLY, Layer, Plan, TrainLayer, UgDesc, UgError, UgInfo,
     UgWarmDesc, ug_warm_start,
     bwd_workspace, desc_of, lib, make_desc, ug_attn_bwd, ug_attn_fwd, ug_attn_fwd_lse, ug_attn_fwd_raster,
-    ug_last_error, ug_permute, ug_permute_rope, ug_plan, ug_plan_export, ug_plan_export_lr, ug_plan_free,
+    ug_last_error, ug_permute, ug_permute_rope, ug_plan, ug_plan_export, ug_plan_export_lr, ug_plan_export_queues, ug_plan_free,
     ug_plan_info, ug_permute_rope_bwd, ug_rope2d, ug_rope2d_bwd, ug_status_str, ug_unpermute)

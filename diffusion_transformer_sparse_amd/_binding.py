@@ -19,7 +19,7 @@ UG_OK, UG_ERR_INVALID_ARGUMENT, UG_ERR_UNSUPPORTED, UG_ERR_OUT_OF_MEMORY, UG_ERR
 UG_F32, UG_BF16 = 0, 1
 UG_PLAN_HOST_ONLY = 1
 
-EXPORTED = ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr", "ug_permute",
+EXPORTED = ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr", "ug_plan_export_queues", "ug_permute",
             "ug_unpermute",
             "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_attn_fwd_lse", "ug_attn_bwd",
             "ug_rope2d_bwd", "ug_permute_rope_bwd", "ug_warm_start", "ug_status_str", "ug_last_error")
@@ -69,6 +69,7 @@ def lib():
         L.ug_plan_info.argtypes = [c_void_p, POINTER(UgInfo)]
         L.ug_plan_export.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
         L.ug_plan_export_lr.argtypes = [c_void_p, c_void_p, c_void_p]
+        L.ug_plan_export_queues.argtypes = [c_void_p, c_void_p, c_void_p]
         L.ug_permute.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
         L.ug_unpermute.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
         L.ug_rope2d.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
@@ -84,7 +85,8 @@ def lib():
         L.ug_status_str.restype = c_char_p
         L.ug_last_error.argtypes = []
         L.ug_last_error.restype = c_char_p
-        for name in ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr", "ug_permute",
+        for name in ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr",
+                     "ug_plan_export_queues", "ug_permute",
                      "ug_unpermute",
                      "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_attn_fwd_lse",
                      "ug_attn_bwd", "ug_rope2d_bwd", "ug_permute_rope_bwd", "ug_warm_start"):
@@ -180,6 +182,15 @@ def ug_plan_export(plan: Plan) -> dict:
     _check("ug_plan_export", lib().ug_plan_export(plan.handle, perm.ctypes.data, win_off.ctypes.data,
                                                   nbr.ctypes.data, nbr_off.ctypes.data))
     return {"perm": perm, "win_off": win_off, "nbr": nbr[:info["n_neighbour_entries"]], "nbr_off": nbr_off}
+
+
+def ug_plan_export_queues(plan: Plan) -> dict:
+    """Per-XCD work queues as [n, 2] (task, batch*head) arrays; task -1 = padding."""
+    info = plan.info
+    attn = np.empty((max(1, info["attn_blocks"]), 2), np.int32)
+    bwd = np.empty((max(1, info["bwd_blocks"]), 2), np.int32)
+    _check("ug_plan_export_queues", lib().ug_plan_export_queues(plan.handle, attn.ctypes.data, bwd.ctypes.data))
+    return {"attn": attn[:info["attn_blocks"]], "bwd": bwd[:info["bwd_blocks"]]}
 
 
 def ug_plan_export_lr(plan: Plan) -> dict:

@@ -599,6 +599,20 @@ ug_status ug_plan_export_lr(ug_plan_t p, int32_t* lr_perm, int32_t* lr_win_off) 
   return UG_OK;
 }
 
+ug_status ug_plan_export_queues(ug_plan_t p, int32_t* attn_items, int32_t* bwd_items) {
+  ug::clear_error();
+  if (!p) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_plan_export_queues: plan is NULL");
+  auto put = [](const std::vector<ug::Block>& b, int32_t* out) {
+    for (size_t i = 0; i < b.size(); ++i) {
+      out[2 * i] = b[i].task;
+      out[2 * i + 1] = b[i].bh;
+    }
+  };
+  if (attn_items) put(p->blocks, attn_items);
+  if (bwd_items) put(p->kblocks, bwd_items);
+  return UG_OK;
+}
+
 const char* ug_status_str(ug_status s) {
   switch (s) {
     case UG_OK: return "UG_OK";

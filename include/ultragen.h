@@ -165,6 +165,18 @@ ug_status ug_plan_export(ug_plan_t plan, int32_t* perm, int32_t* win_off, int32_
 ug_status ug_plan_export_lr(ug_plan_t plan, int32_t* lr_perm, int32_t* lr_win_off);
 
 /*
+ * ug_plan_export_queues: the per-XCD work queues (either pointer may be
+ * NULL), as (task, batch*head) pairs; task = -1 marks padding.
+ *  attn_items int32[2 * info.attn_blocks]  query tiles of the attention
+ *                                          forward and of the backward's dQ pass
+ *  bwd_items  int32[2 * info.bwd_blocks]   key tiles of the dK/dV pass
+ * Item k*8 + x is the k-th item of XCD x's queue.  Each queue holds its
+ * items first and padding only after them, which the persistent grids rely
+ * on (a cursor on padding means that queue is empty).
+ */
+ug_status ug_plan_export_queues(ug_plan_t plan, int32_t* attn_items, int32_t* bwd_items);
+
+/*
  * ug_permute: x_perm = x_raster with HR rows gathered into window-first
  * order (关键设计 1; gist.science summary 2.A, window-first token
  * permutation); text and LR rows copied unchanged.  Out of place:

@@ -150,14 +150,29 @@ def test_null_arguments():
     assert lib.ug_plan_free(None) == 0
 
 
-def test_block_order_covers_every_task_once():
-    """Every (task, batch*head) pair appears exactly once in the workgroup order;
-    the rest of the entries are idle."""
-    w = WORKLOADS["4k"]
+@pytest.mark.parametrize("name", ["tiny", "tiny_masked", "small_ragged", "small_ragged_corr", "1k", "4k", "ragged",
+                                  "4k_corr"])
+def test_work_queues_cover_every_item_once(name):
+    """The per-XCD work queues (item k*8 + x is the k-th of XCD x's queue) hold
+    every (task, batch*head) pair exactly once, each queue's items before its
+    padding: the persistent grids take a cursor on padding to mean that queue
+    is empty, so a real item after padding would never run."""
+    w = WORKLOADS[name]
     p = _host_plan(w)
     info = p.info
-    assert info["attn_blocks"] >= info["attn_tasks"] * w.heads
-    assert info["attn_blocks"] - info["attn_tasks"] * w.heads < 8 * 64
+    bh = w.batch * w.heads
+    q = U.ug_plan_export_queues(p)
+    for items, n_tasks in ((q["attn"], info["attn_tasks"]), (q["bwd"], info["bwd_key_tasks"])):
+        assert len(items) % 8 == 0
+        per_xcd = items.reshape(-1, 8, 2)
+        for x in range(8):
+            real = per_xcd[:, x, 0] >= 0
+            n_real = int(real.sum())
+            assert real[:n_real].all() and not real[n_real:].any(), f"padding inside XCD {x}'s queue"
+        r = items[items[:, 0] >= 0].astype(np.int64)
+        assert r[:, 0].max() < n_tasks and r[:, 1].min() >= 0 and r[:, 1].max() < bh
+        keys = r[:, 0] * bh + r[:, 1]
+        assert len(np.unique(keys)) == len(keys) == n_tasks * bh
 
 
 @pytest.mark.parametrize("field,value", [("batch", 0), ("hr_h", 0), ("lr_w", 0), ("rho", 0), ("channels", 12),
