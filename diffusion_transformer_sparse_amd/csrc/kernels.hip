@@ -41,7 +41,7 @@ using ug::host::tensor_bytes;
 // non-temporal 16-byte vectors; each thread owns one 16-byte column of
 // kGatherRows consecutive rows and has all of them in flight at once.
 // ---------------------------------------------------------------------------
-constexpr int kGatherRows = 4;  // token rows per workgroup
+constexpr int kGatherRows = 2;  // token rows per workgroup (2 measured fastest of 1, 2, 4, 8, 16)
 
 __global__ __launch_bounds__(1024) void row_gather_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                           int32_t L, int32_t T, int32_t N, int32_t units,
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(1024) void row_gather_kernel(const u32x4* __restric
 // head) of kRopeRows consecutive rows in both Q and K, all loads in flight at
 // once; every byte is read and written once, with non-temporal accesses.
 // ---------------------------------------------------------------------------
-constexpr int kRopeRows = 4;  // token rows per workgroup
+constexpr int kRopeRows = 2;  // token rows per workgroup (2 measured fastest of 1, 2, 4, 8, 16)
 
 // (cos, sin) of the angle, or of its negation for the transpose (inverse)
 // rotation that carries gradients back through the RoPE.
