@@ -170,9 +170,9 @@ def run_layer_bwd(U, w, host=True):
     p = U.ug_plan(U.desc_of(w))
     q, k, v, do = inputs(w)
     layer = U.TrainLayer(p)
-    out = torch.empty_like(q)
+    out = torch.full_like(q, float("nan"))  # NaN until written: a skipped work item shows up
     layer.forward(q, k, v, out)
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
     layer.backward(do, dq, dk, dv)
     torch.cuda.synchronize()
     if not host:
@@ -243,8 +243,11 @@ def test_full_size_backward_sampled(U, name):
     512x512); the oracle recomputes dq of sampled query rows
     (corner, edge, interior HR, text, LR) and dk, dv of sampled HR key rows
     (with lr_mode 1 also LR key rows) one by one."""
+    import torch
     w = WL.WORKLOADS[name]
-    _, (_, dq_d, dk_d, dv_d) = run_layer_bwd(U, w, host=False)
+    _, (out_d, dq_d, dk_d, dv_d) = run_layer_bwd(U, w, host=False)
+    for t, n in ((out_d, "out"), (dq_d, "dq"), (dk_d, "dk"), (dv_d, "dv")):  # every element written
+        assert bool(torch.isfinite(t).all()), f"{name}: {n} has unwritten (NaN) elements"
     geo = O.geometry_of(w)
     T, W, H = w.n_text, w.hr_w, w.hr_h
     qrows = np.array([0, T - 1, T, T + 15 * W + 16, T + 100 * W + 37, T + w.n_hr - 1, T + w.n_hr,

@@ -151,12 +151,13 @@ def sample_rows(w, seed=0):
 def test_full_size_sampled_rows(U, name, fused):
     """The bench's launch configuration (fused layer) at full size; the
     oracle recomputes sampled rows one by one (text, corner/edge/interior HR
-    windows, LR)."""
+    windows, LR).  The output starts as NaN, so the final finiteness check
+    shows that every row of every head was written (no work item skipped)."""
     import torch
     w = WL.WORKLOADS[name]
     p = plan_of(U, w)
     q, k, v = qkv_device(w)
-    out = torch.empty_like(q)
+    out = torch.full_like(q, float("nan"))
     U.Layer(p, fused=fused)(q, k, v, out)
     torch.cuda.synchronize()
     geo = O.geometry_of(w)
