@@ -296,7 +296,7 @@ __device__ __forceinline__ void run_queue(Item item_fn) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup per query tile (the forward's tasks), 8 waves x 32
+// dQ: per query tile (the forward's tasks, taken from the queues), 8 waves x 32
 // queries.  Per wave and 64-key tile (K, V in two-slot LDS rings):
 //   S^T  = K Q^T     (A: K rows from LDS, B: the wave's Q in registers)
 //   dP^T = V dO^T    (A: V rows from LDS, B: the wave's dO in registers)
