@@ -39,12 +39,16 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (vector / MFMA f32 dense)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "diffusion_transformer_sparse_amd", "csrc", "kernels.hip")
+# the attention kernel and the plan that orders its work (the order sets the L2 re-fetches)
+KERNEL_SRCS = [os.path.join(ROOT, "diffusion_transformer_sparse_amd", "csrc", n) for n in ("kernels.hip", "plan.cpp")]
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):

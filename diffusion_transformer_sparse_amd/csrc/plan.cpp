@@ -362,15 +362,15 @@ void build_key_tasks(ug_plan_s& p) {
 // Per-XCD work queues.  Each XCD has its own L2, so the order is built per
 // XCD: every XCD gets a queue whose long items (query tiles with many more
 // key tiles than the average, i.e. text rows) come first, longest first, then
-// a contiguous slice of the remaining items in (batch, head, tile) order, so
-// that tiles of one head that share neighbour windows and the LR keys run on
-// the same L2.  Queues are balanced by key-tile count and interleaved (item
+// a contiguous slice of the remaining items in (batch, head, locality) order,
+// so that tiles of one head that share neighbour windows and the LR keys run
+// on the same L2 (locality: the attention's window tiles in Z-order).  Queues are balanced by key-tile count and interleaved (item
 // k * 8 + x is the k-th of XCD x's queue); short queues are padded with idle
 // items.  The attention forward's persistent workgroups take items from these
 // queues dynamically; the backward launches one workgroup per item, which the
 // hardware hands to XCD i % 8 in the same interleaved order.
 std::vector<ug::Block> order_blocks(const std::vector<ug::Task>& tasks, const std::vector<ug::Range>& ranges,
-                                    int64_t BH) {
+                                    int64_t BH, const std::vector<int64_t>& locality) {
   const int X = ug::kXcds;
   std::vector<int64_t> cost(tasks.size());
   double mean = 0;
@@ -379,6 +379,9 @@ std::vector<ug::Block> order_blocks(const std::vector<ug::Task>& tasks, const st
   std::vector<int32_t> long_tasks, normal_tasks;
   for (size_t t = 0; t < tasks.size(); ++t)
     (double(cost[t]) > 2.0 * mean ? long_tasks : normal_tasks).push_back(int32_t(t));
+  if (!locality.empty())
+    std::stable_sort(normal_tasks.begin(), normal_tasks.end(),
+                     [&](int32_t a, int32_t b) { return locality[a] < locality[b]; });
 
   std::vector<std::vector<ug::Block>> q(X);
   std::vector<int64_t> load(X, 0);
@@ -411,10 +414,35 @@ std::vector<ug::Block> order_blocks(const std::vector<ug::Task>& tasks, const st
   return blocks;
 }
 
+// Morton (Z-order) code of a window's (row, column): consecutive codes stay
+// in compact 2D blocks, so the query tiles that run at the same time on one
+// XCD share more of their neighbour windows' K/V tiles in its L2.
+int64_t morton(int32_t y, int32_t x) {
+  int64_t m = 0;
+  for (int b = 0; b < 16; ++b)
+    m |= (int64_t((y >> b) & 1) << (2 * b + 1)) | (int64_t((x >> b) & 1) << (2 * b));
+  return m;
+}
+
 void build_blocks(ug_plan_s& p) {
   const int64_t BH = int64_t(p.d.batch) * p.d.heads;
-  p.blocks = order_blocks(p.tasks, p.ranges, BH);
-  p.kblocks = order_blocks(p.ktasks, p.kranges, BH);
+  // Query tiles of HR windows in Z-order over the window grid (tiles of one
+  // window in row order), then the LR tiles, text tiles first.
+  std::vector<int64_t> locality(p.tasks.size());
+  for (size_t t = 0; t < p.tasks.size(); ++t) {
+    const int64_t q0 = p.tasks[t].q0;
+    if (q0 < p.T) {
+      locality[t] = -1;
+    } else if (q0 < p.T + p.N) {
+      const int32_t j = int32_t(q0 - p.T);
+      const int32_t w = int32_t(std::upper_bound(p.win_off.begin(), p.win_off.end(), j) - p.win_off.begin()) - 1;
+      locality[t] = morton(w / p.gx, w % p.gx) * (int64_t(1) << 20) + (j - p.win_off[w]);
+    } else {
+      locality[t] = (int64_t(1) << 62) + q0;
+    }
+  }
+  p.blocks = order_blocks(p.tasks, p.ranges, BH, locality);
+  p.kblocks = order_blocks(p.ktasks, p.kranges, BH, {});
 }
 
 template <typename T>
