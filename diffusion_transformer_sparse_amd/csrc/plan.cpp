@@ -406,6 +406,21 @@ std::vector<ug::Block> order_blocks(const std::vector<ug::Task>& tasks, const st
       q[x].push_back({t, int32_t(bh)});
       load[x] += cost[t];
     }
+  // The queues end with their shortest items (those under 80% of the median
+  // normal item, e.g. the LR query tiles), so the last items the CUs take are
+  // short and they run out of work closer together.
+  if (!normal_tasks.empty()) {
+    std::vector<int64_t> nc;
+    for (int32_t t : normal_tasks) nc.push_back(cost[t]);
+    std::nth_element(nc.begin(), nc.begin() + nc.size() / 2, nc.end());
+    const double short_cost = 0.8 * double(nc[nc.size() / 2]);
+    for (auto& qq : q) {
+      const size_t first_normal = std::min(qq.size(), size_t(std::count_if(
+          qq.begin(), qq.end(), [&](const ug::Block& b) { return double(cost[b.task]) > 2.0 * mean; })));
+      std::stable_partition(qq.begin() + first_normal, qq.end(),
+                            [&](const ug::Block& b) { return double(cost[b.task]) >= short_cost; });
+    }
+  }
   size_t len = 0;
   for (const auto& qq : q) len = std::max(len, qq.size());
   std::vector<ug::Block> blocks(len * X, ug::Block{-1, 0});
