@@ -251,6 +251,20 @@ def test_attention_queue_cursors_reused_and_concurrent(U):
     torch.cuda.synchronize()
     for j, out in enumerate(outs):
         assert torch.equal(bits(out), bits(ref)), f"concurrent launch {j}"
+    # two plans (different shapes, their own cursors) at the same time
+    w2 = WL.WORKLOADS["small_ragged"]
+    p2 = plan_of(U, w2)
+    q2, k2, v2 = qkv_device(w2)
+    ref2 = U.ug_attn_fwd(p2, q2, k2, v2)
+    torch.cuda.synchronize()
+    o1, o2 = torch.empty_like(ref), torch.empty_like(ref2)
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            U.ug_attn_fwd(p, q, k, v, o1)
+        with torch.cuda.stream(s2):
+            U.ug_attn_fwd(p2, q2, k2, v2, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(o1), bits(ref)) and torch.equal(bits(o2), bits(ref2))
 
 
 # ------------------------------------------------------------------ edge cases
