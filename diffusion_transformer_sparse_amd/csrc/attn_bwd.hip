@@ -202,44 +202,65 @@ __device__ __forceinline__ void store_block(const f32x16 (&acc)[D / 32], float s
 
 // ---------------------------------------------------------------------------
 // prep: lse2[bh][row] = lse * log2(e) and delta[bh][row] = sum_d dO * O, in
-// fp32, for rows < L; rows L .. stat_rows-1 are written as zeros.  Each thread
-// owns one 16-byte column chunk of kPrepRows rows; the D/8 chunks of one head
-// are consecutive lanes of a wave and are summed with shuffles.
+// fp32, for rows < L; rows L .. stat_rows-1 are written as zeros.  A
+// workgroup takes kPrepRows rows of up to kPrepHeads heads (grid z covers the
+// head groups): each thread owns one 16-byte column chunk and has four rows
+// of O and dO in flight at once; the D/8 chunks of one head are consecutive
+// lanes and are summed with shuffles.  The sums are collected in LDS, so each
+// head's statistics leave as one contiguous run of kPrepRows floats.
 // ---------------------------------------------------------------------------
-constexpr int kPrepRows = 4;
+constexpr int kPrepRows = 64;
+constexpr int kPrepHeads = 64;
+constexpr int kPrepInFlight = 4;
 
 template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ d_o,
-                                                       const float* __restrict__ lse, float* __restrict__ lse2,
-                                                       float* __restrict__ delta, int32_t L, int32_t Lp,
-                                                       int32_t heads) {
+__global__ __launch_bounds__(1024) void bwd_prep_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ d_o,
+                                                        const float* __restrict__ lse, float* __restrict__ lse2,
+                                                        float* __restrict__ delta, int32_t L, int32_t Lp,
+                                                        int32_t heads) {
   constexpr int C = D / 8;  // chunks per head
-  const int32_t units = heads * C;
+  __shared__ float s_sum[kPrepHeads * kPrepRows];  // [head of the group][row]
+  const int32_t h0 = blockIdx.z * kPrepHeads;
+  const int32_t gh = min(kPrepHeads, heads - h0);  // heads of this group
+  const int32_t units = gh * C;
   const int32_t b = blockIdx.y;
-  const int64_t boff = int64_t(b) * L * heads * D;
-  for (int r = 0; r < kPrepRows; ++r) {
-    const int32_t row = blockIdx.x * kPrepRows + r;
-    if (row >= Lp) break;
-    for (int32_t c0 = 0; c0 < units; c0 += 256) {  // uniform trip count: every lane shuffles
-      const int32_t c = c0 + int32_t(threadIdx.x);
-      float sum = 0.f;
-      if (c < units && row < L) {
-        const int64_t e = boff + int64_t(row) * heads * D + int64_t(c) * 8;
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + e);
-        const bf16x8 y = *reinterpret_cast<const bf16x8*>(d_o + e);
+  const int32_t row0 = blockIdx.x * kPrepRows;
+  const int64_t boff = int64_t(b) * L * heads * D + int64_t(h0) * D;
+  for (int32_t c0 = 0; c0 < units; c0 += blockDim.x) {  // uniform trip count: every lane shuffles
+    const int32_t c = c0 + int32_t(threadIdx.x);
+    for (int32_t rb = 0; rb < kPrepRows; rb += kPrepInFlight) {
+      bf16x8 x[kPrepInFlight], y[kPrepInFlight];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) sum = fmaf(float(x[k]), float(y[k]), sum);
+      for (int r = 0; r < kPrepInFlight; ++r) {
+        const int32_t row = row0 + rb + r;
+        if (c < units && row < L) {
+          const int64_t e = boff + int64_t(row) * heads * D + int64_t(c) * 8;
+          x[r] = *reinterpret_cast<const bf16x8*>(o + e);
+          y[r] = *reinterpret_cast<const bf16x8*>(d_o + e);
+        }
       }
 #pragma unroll
-      for (int m = C / 2; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, C);
-      if (c < units && c % C == 0) {
-        const int32_t h = c / C;
-        const int64_t s = (int64_t(b) * heads + h) * Lp + row;
-        const bool in = row < L;
-        delta[s] = in ? sum : 0.f;
-        lse2[s] = in ? lse[(int64_t(b) * heads + h) * L + row] * kLog2e : 0.f;
+      for (int r = 0; r < kPrepInFlight; ++r) {
+        const int32_t row = row0 + rb + r;
+        float sum = 0.f;
+        if (c < units && row < L) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) sum = fmaf(float(x[r][k]), float(y[r][k]), sum);
+        }
+#pragma unroll
+        for (int m = C / 2; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, C);
+        if (c < units && c % C == 0) s_sum[(c / C) * kPrepRows + rb + r] = sum;
       }
     }
+  }
+  __syncthreads();
+  for (int32_t i = threadIdx.x; i < gh * kPrepRows; i += blockDim.x) {
+    const int32_t h = h0 + i / kPrepRows, row = row0 + i % kPrepRows;
+    if (row >= Lp) continue;
+    const int64_t s = (int64_t(b) * heads + h) * Lp + row;
+    const bool in = row < L;
+    delta[s] = in ? s_sum[i] : 0.f;
+    lse2[s] = in ? lse[(int64_t(b) * heads + h) * L + row] * kLog2e : 0.f;
   }
 }
 
@@ -558,8 +579,12 @@ template <int D>
 void launch_bwd(ug_plan_t p, BwdParams bp, const __bf16* o, const float* lse, float* lse2, float* delta,
                 hipStream_t s) {
   const int32_t Lp = int32_t(p->stat_rows());
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(unsigned((Lp + kPrepRows - 1) / kPrepRows), unsigned(p->d.batch)),
-                     dim3(256), 0, s, o, bp.d_o, lse, lse2, delta, int32_t(p->L), Lp, p->d.heads);
+  const int32_t units = std::min(p->d.heads, kPrepHeads) * (D / 8);
+  const unsigned prep_threads = unsigned(std::min(1024, (units + 63) / 64 * 64));
+  hipLaunchKernelGGL((bwd_prep_kernel<D>),
+                     dim3(unsigned((Lp + kPrepRows - 1) / kPrepRows), unsigned(p->d.batch),
+                          unsigned((p->d.heads + kPrepHeads - 1) / kPrepHeads)),
+                     dim3(prep_threads), 0, s, o, bp.d_o, lse, lse2, delta, int32_t(p->L), Lp, p->d.heads);
   bp.tasks = p->d_tasks;
   bp.ranges = p->d_ranges;
   bp.blocks = p->d_blocks;
