@@ -370,7 +370,7 @@ void build_key_tasks(ug_plan_s& p) {
 // queues dynamically; the backward launches one workgroup per item, which the
 // hardware hands to XCD i % 8 in the same interleaved order.
 std::vector<ug::Block> order_blocks(const std::vector<ug::Task>& tasks, const std::vector<ug::Range>& ranges,
-                                    int64_t BH, const std::vector<int64_t>& locality) {
+                                    int64_t BH, const std::vector<int64_t>& locality, bool group_long) {
   const int X = ug::kXcds;
   std::vector<int64_t> cost(tasks.size());
   double mean = 0;
@@ -385,15 +385,30 @@ std::vector<ug::Block> order_blocks(const std::vector<ug::Task>& tasks, const st
 
   std::vector<std::vector<ug::Block>> q(X);
   std::vector<int64_t> load(X, 0);
-  std::vector<ug::Block> longs;
-  for (int64_t bh = 0; bh < BH; ++bh)
-    for (int32_t t : long_tasks) longs.push_back({t, int32_t(bh)});
-  std::stable_sort(longs.begin(), longs.end(),
-                   [&](const ug::Block& a, const ug::Block& b) { return cost[a.task] > cost[b.task]; });
-  for (const auto& b : longs) {
-    const int x = int(std::min_element(load.begin(), load.end()) - load.begin());
-    q[x].push_back(b);
-    load[x] += cost[b.task];
+  std::vector<int32_t> by_cost = long_tasks;
+  std::stable_sort(by_cost.begin(), by_cost.end(), [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
+  if (group_long && BH >= X) {
+    // One head's long items together on one XCD, longest first: they start
+    // at about the same time and share the rows they all stream (every key
+    // of the head) in that XCD's L2.
+    int64_t group = 0;
+    for (int32_t t : long_tasks) group += cost[t];
+    for (int64_t bh = 0; bh < BH; ++bh) {
+      const int x = int(std::min_element(load.begin(), load.end()) - load.begin());
+      for (int32_t t : by_cost) q[x].push_back({t, int32_t(bh)});
+      load[x] += group;
+    }
+  } else {
+    std::vector<ug::Block> longs;
+    for (int64_t bh = 0; bh < BH; ++bh)
+      for (int32_t t : long_tasks) longs.push_back({t, int32_t(bh)});
+    std::stable_sort(longs.begin(), longs.end(),
+                     [&](const ug::Block& a, const ug::Block& b) { return cost[a.task] > cost[b.task]; });
+    for (const auto& b : longs) {
+      const int x = int(std::min_element(load.begin(), load.end()) - load.begin());
+      q[x].push_back(b);
+      load[x] += cost[b.task];
+    }
   }
   int64_t total = std::accumulate(load.begin(), load.end(), int64_t(0));
   for (int64_t bh = 0; bh < BH; ++bh)
@@ -456,8 +471,11 @@ void build_blocks(ug_plan_s& p) {
       locality[t] = (int64_t(1) << 62) + q0;
     }
   }
-  p.blocks = order_blocks(p.tasks, p.ranges, BH, locality);
-  p.kblocks = order_blocks(p.ktasks, p.kranges, BH, {});
+  p.blocks = order_blocks(p.tasks, p.ranges, BH, locality, true);
+  // The dK/dV pass's long items (key tiles every query sees) stay spread
+  // over the XCDs: grouped, 18 of them stream the same rows at once and the
+  // pass ran 2.5-3% slower although it fetched less than half as much.
+  p.kblocks = order_blocks(p.ktasks, p.kranges, BH, {}, false);
 }
 
 template <typename T>
