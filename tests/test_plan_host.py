@@ -175,6 +175,46 @@ def test_work_queues_cover_every_item_once(name):
         assert len(np.unique(keys)) == len(keys) == n_tasks * bh
 
 
+def test_work_queue_order_4k():
+    """The attention's work order at 4K (performance choices, pinned so they
+    do not drift): each queue starts with long items (the text query tiles),
+    a head's long items all sit on one XCD, the window tiles follow in
+    Z-order of their window, and each queue ends with its short items (the
+    LR query tiles)."""
+    w = WORKLOADS["4k"]
+    p = _host_plan(w)
+    T, N = w.n_text, w.n_hr
+    ex = U.ug_plan_export(p)
+    gx = w.hr_w // w.window
+    q = U.ug_plan_export_queues(p)["attn"].reshape(-1, 8, 2)
+    # task ids: text tiles, then LR tiles, then one per window (4K: whole 256-token windows)
+    n_text_tiles, n_lr_tiles = -(-T // 256), -(-w.n_lr // 256)
+    kind = lambda t: "text" if t < n_text_tiles else "lr" if t < n_text_tiles + n_lr_tiles else "win"
+    xcd_of_text_head = {}
+    for x in range(8):
+        items = [(int(t), int(bh)) for t, bh in q[:, x] if t >= 0]
+        kinds = [kind(t) for t, _ in items]
+        n_long = kinds.count("text")
+        assert kinds[:n_long] == ["text"] * n_long, f"XCD {x}: long items first"
+        n_lr = kinds.count("lr")
+        assert kinds[len(kinds) - n_lr:] == ["lr"] * n_lr, f"XCD {x}: short items last"
+        for t, bh in items[:n_long]:
+            assert xcd_of_text_head.setdefault(bh, x) == x, f"head {bh}'s long items on two XCDs"
+        # window tiles of one head follow in increasing Z-order of their window
+        def morton(wi):
+            y, xx, m = wi // gx, wi % gx, 0
+            for b in range(8):
+                m |= ((y >> b) & 1) << (2 * b + 1) | ((xx >> b) & 1) << (2 * b)
+            return m
+        last = {}
+        for t, bh in items:
+            if kind(t) == "win":
+                z = morton(t - n_text_tiles - n_lr_tiles)
+                assert z > last.get(bh, -1), f"XCD {x}: head {bh} windows out of Z-order"
+                last[bh] = z
+    assert len(xcd_of_text_head) == w.batch * w.heads
+
+
 @pytest.mark.parametrize("field,value", [("batch", 0), ("hr_h", 0), ("lr_w", 0), ("rho", 0), ("channels", 12),
                                          ("channels", 0), ("dtype", 5), ("alpha", 1.5), ("alpha", -0.1),
                                          ("alpha", float("nan")), ("sharpen", -1.0), ("sharpen", float("inf"))])
