@@ -180,6 +180,20 @@ def run_layer_bwd(U, w, host=True):
     return p, [to_host_f64(x, w.dtype) for x in (out, dq, dk, dv)]
 
 
+def test_layer_backward_two_images_many_heads(U):
+    """TrainLayer backward at batch 2 x 8 heads (the work queues group each
+    head's long tiles on one XCD): first and last head of both images
+    against the oracle."""
+    w = WL.WORKLOADS["ragged_b2"]
+    _, (_, dq, dk, dv) = run_layer_bwd(U, w)
+    for b in range(w.batch):
+        for h, geo, (qh, kh, vh, doh) in oracle_heads(w, (0, w.heads - 1), b):
+            rq, rk, rv = O.backward_head(geo, qh, kh, vh, doh, w.rope_theta)
+            grad_close(dq[b][:, h], rq, w, f"ragged_b2 image {b} dq h{h}")
+            grad_close(dk[b][:, h], rk, w, f"ragged_b2 image {b} dk h{h}")
+            grad_close(dv[b][:, h], rv, w, f"ragged_b2 image {b} dv h{h}")
+
+
 @pytest.mark.parametrize("name", SMALL_BWD + ["1k"])
 def test_layer_backward_matches_oracle(U, name):
     """TrainLayer (raster in, raster out: RoPE, permutation, attention and

@@ -133,6 +133,25 @@ def test_full_layer_matches_oracle(U, name, fused):
         assert_close(seg_errors(got[:, h], ref, w), tol_of(w), f"{name} head {h}")
 
 
+def test_two_images_many_heads(U):
+    """Batch 2 x 8 heads on a ragged 72x88 grid: batch*heads = 16, so the
+    work queues keep each head's long tiles on one XCD.  The fused layer
+    against the oracle for every head of both images."""
+    import torch
+    w = WL.WORKLOADS["ragged_b2"]
+    p = plan_of(U, w)
+    q, k, v = qkv_device(w)
+    out = torch.full_like(q, float("nan"))
+    U.Layer(p, fused=True)(q, k, v, out)
+    torch.cuda.synchronize()
+    got = to_host_f64(out, w.dtype)
+    geo = O.geometry_of(w)
+    for b in range(w.batch):
+        for h in range(w.heads):
+            ref = O.forward_head(geo, *(WL.head_f64(w, t, h, b) for t in (WL.Q, WL.K, WL.V)), w.rope_theta)
+            assert_close(seg_errors(got[b][:, h], ref, w), tol_of(w), f"ragged_b2 image {b} head {h}")
+
+
 def sample_rows(w, seed=0):
     rng = np.random.default_rng(seed)
     T, N, L, H, W = w.n_text, w.n_hr, w.seq_len, w.hr_h, w.hr_w

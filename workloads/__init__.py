@@ -96,6 +96,9 @@ WORKLOADS = {
     "small_ragged_corr": Workload("small_ragged_corr", 11, 40, 56, 10, 14, 40, 3, 128, "bf16", lr_mode=1),
     "tiny_masked_corr": Workload("tiny_masked_corr", 12, 48, 48, 12, 12, 16, 2, 64, "f32", lr_mode=1),
     "ragged_corr_f32": Workload("ragged_corr_f32", 13, 37, 45, 11, 13, 9, 2, 64, "f32", lr_mode=1),
+    # two images of 8 heads: batch*heads = 16, so the work queues group each
+    # head's long items on one XCD; ragged 72x88 grid
+    "ragged_b2": Workload("ragged_b2", 14, 72, 88, 18, 22, 64, 8, 128, "bf16", batch=2),
 }
 
 
