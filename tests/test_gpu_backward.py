@@ -251,7 +251,7 @@ def test_backward_is_deterministic(U):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["4k", "4k_corr", "ragged", "8k"])
+@pytest.mark.parametrize("name", ["4k", "4k_corr", "ragged", "8k", "4k_d64"])
 def test_full_size_backward_sampled(U, name):
     """A layer's backward at full size (256x256, the ragged 250x380 grid,
     512x512); the oracle recomputes dq of sampled query rows

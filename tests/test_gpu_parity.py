@@ -166,7 +166,8 @@ def sample_rows(w, seed=0):
 
 
 @pytest.mark.parametrize("name,fused", [("2k", True), ("ragged", True), ("4k", True), ("4k", False),
-                                        ("8k", True), ("4k_corr", True), ("4k_corr", False)])
+                                        ("8k", True), ("4k_corr", True), ("4k_corr", False), ("4k_d64", True),
+                                        ("4k_r2", True)])
 def test_full_size_sampled_rows(U, name, fused):
     """The bench's launch configuration (fused layer) at full size; the
     oracle recomputes sampled rows one by one (text, corner/edge/interior HR

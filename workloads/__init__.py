@@ -99,6 +99,10 @@ WORKLOADS = {
     # two images of 8 heads: batch*heads = 16, so the work queues group each
     # head's long items on one XCD; ragged 72x88 grid
     "ragged_b2": Workload("ragged_b2", 14, 72, 88, 18, 22, 64, 8, 128, "bf16", batch=2),
+    # the 4K layer with head_dim 64 (the D = 64 kernels at full size) and with
+    # radius 2 (5x5 windows: 25 HR ranges per query tile)
+    "4k_d64": Workload("4k_d64", 15, 256, 256, 64, 64, 512, 24, 64, "bf16"),
+    "4k_r2": Workload("4k_r2", 16, 256, 256, 64, 64, 512, 24, 128, "bf16", radius=2),
 }
 
 
