@@ -14,7 +14,7 @@ from tests.gpu_util import (assert_close, qkv_device, seg_errors, to_device, to_
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ["tiny", "tiny_masked", "small_ragged", "small_d64", "small_ragged_f32", "1k"]
+SMALL = ["tiny", "tiny_masked", "small_ragged", "small_d64", "small_ragged_f32", "small_f32_d128", "1k"]
 # corresponding-LR variant (lr_mode 1): LR rows permuted window-first too
 CORR = ["tiny_masked_corr", "small_ragged_corr", "ragged_corr_f32"]
 

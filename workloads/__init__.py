@@ -103,6 +103,8 @@ WORKLOADS = {
     # radius 2 (5x5 windows: 25 HR ranges per query tile)
     "4k_d64": Workload("4k_d64", 15, 256, 256, 64, 64, 512, 24, 64, "bf16"),
     "4k_r2": Workload("4k_r2", 16, 256, 256, 64, 64, 512, 24, 128, "bf16", radius=2),
+    # fp32 with head_dim 128 (the fp32 D = 128 attention kernel), ragged grid
+    "small_f32_d128": Workload("small_f32_d128", 17, 40, 56, 10, 14, 40, 3, 128, "f32"),
 }
 
 
