@@ -189,7 +189,8 @@ def test_full_size_sampled_rows(U, name, fused):
     assert torch.isfinite(out.float()).all()
 
 
-@pytest.mark.parametrize("name", ["tiny", "small_ragged", "small_d64", "small_ragged_f32", "1k", "ragged"] + CORR)
+@pytest.mark.parametrize("name", ["tiny", "small_ragged", "small_d64", "small_ragged_f32", "small_f32_d128", "1k",
+                                  "ragged"] + CORR)
 def test_fused_entry_points_bit_exact(U, name):
     """ug_permute_rope == ug_permute + ug_rope2d and ug_attn_fwd_raster ==
     ug_attn_fwd + ug_unpermute, bit for bit."""
@@ -209,7 +210,8 @@ def test_fused_entry_points_bit_exact(U, name):
     assert torch.equal(as_bits(o_fused), as_bits(o_sep))
 
 
-@pytest.mark.parametrize("name", ["tiny", "small_ragged", "small_d64", "small_ragged_f32", "1k", "ragged"] + CORR
+@pytest.mark.parametrize("name", ["tiny", "small_ragged", "small_d64", "small_ragged_f32", "small_f32_d128", "1k",
+                                  "ragged"] + CORR
                          + ["edge:" + c for c in ("batch2", "no_lr", "no_text", "corr_batch2", "corr_lr_overhang")])
 def test_permute_rope_bwd_bit_exact(U, name):
     """ug_permute_rope_bwd == ug_rope2d_bwd + ug_unpermute of dq and dk, bit
