@@ -296,7 +296,7 @@ __global__ __launch_bounds__(1024) void permute_rope_kernel(const T* __restrict_
 //                  8*(j/4) + 4*g + j%4 (j < 16) of each 32-key block, so a
 //                  query's softmax statistics are lane-local except for one
 //                  exchange between the two lane halves (v_permlane32_swap).
-//   P = exp2(S*scale*log2e - m), m the running maximum (fp32).
+//   P = exp2(S*scale*log2e - m), m a softmax reference (fp32, log2 units).
 //   O^T += V^T P^T A = V^T read from the [key][dim] V tile with the LDS
 //                  transpose read ds_read_b64_tr_b16: in each 16-lane group,
 //                  lane j gets dim j of four keys, so two reads give a lane
@@ -306,16 +306,27 @@ __global__ __launch_bounds__(1024) void permute_rope_kernel(const T* __restrict_
 // LDS rows are unpadded; 16-byte chunks are XOR-swizzled by row so the
 // K-operand reads (32 rows, one chunk) and the transpose reads (4 rows,
 // 64 bytes) are bank-conflict free.
-// Software pipeline: K runs one tile ahead of V in two LDS rings, so while a
-// wave exponentiates tile i's scores (VALU) it already issues tile i+1's
-// QK^T MFMAs, then tile i's PV MFMAs; the MFMA and VALU pipes overlap inside
-// one wave.  The running maximum is only moved when a tile's maximum exceeds
-// it by more than 8 (log2 units); the final normalisation uses the same
-// reference, so the result is unchanged while the O^T registers are
-// rescaled rarely.  bf16: v_mfma_f32_32x32x16_bf16, P rounded to bf16 for
-// the PV product and the row sum taken over the same rounded P; fp32:
-// v_mfma_f32_32x32x2_f32.  The output goes through LDS so every row is
-// written with full 16-byte stores.
+//
+// bf16 (v_mfma_f32_32x32x16_bf16), attn_item_bf16: a three-stage software
+// pipeline.  Step i runs QK^T of tile i+1, the exponentials of tile i and PV
+// of tile i-1 side by side, as one MFMA per slot with one or two weights of
+// tile i per slot, so the VALU work is spread evenly over every MFMA (VALU
+// instructions next to MFMAs cost MFMA time once a slot holds more than a
+// few).  The softmax reference is not a running maximum: it starts 8 above
+// the first tile's exact maximum and only moves when a later tile could hold
+// large weights, which the row sum detects exactly: a lane's partial sum of
+// its 32 weights of a tile is below 2^8 only if every weight is.  When some
+// lane's partial sum reaches 2^8, the reference moves up by a whole number
+// of octaves (so the rescaling of what was accumulated is exact), to 8 above
+// the tile's maximum, and the tile's weights are recomputed before the next
+// step uses them.  P is rounded to bf16 for the PV product, and the row sum
+// is taken over the same rounded weights.
+// fp32 (v_mfma_f32_32x32x2_f32), attn_item_f32: a two-stage pipeline (QK^T
+// of tile i+1 beside the exponentials of tile i, then PV of tile i beside the
+// maximum of tile i+1) with a running maximum moved only when a tile's
+// maximum exceeds it by more than 8.
+// The output goes through LDS so every row is written with full 16-byte
+// stores.
 // Persistent grid: one workgroup per CU takes query tiles from the plan's
 // eight per-XCD queues (the workgroup order, XCD x's queue at items x,
 // x + 8, ...) through an atomic cursor per queue, its own XCD's queue first,
@@ -441,11 +452,11 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const char* ktile, const
 typedef __attribute__((address_space(4))) const AttnParams* KArgs;
 __device__ __forceinline__ KArgs kernel_args() { return opaque_args<AttnParams>(); }
 
-// One query tile (plan item `item`) of the attention.
-template <typename T, int D>
-__device__ __forceinline__ void attn_item(KArgs kp, int32_t item, char* smem, ug::Range* s_rng) {
+// One fp32 query tile (plan item `item`) of the attention.
+template <int D>
+__device__ __forceinline__ void attn_item_f32(KArgs kp, int32_t item, char* smem, ug::Range* s_rng) {
+  using T = float;
   using Lds = AttnLds<T, D>;
-  constexpr bool kBF = Lds::kBF;
   constexpr int TB = Lds::kTileBytes;
   // K ring at [0, 2*TB), V ring at [2*TB, 4*TB)
 
@@ -476,16 +487,10 @@ __device__ __forceinline__ void attn_item(KArgs kp, int32_t item, char* smem, ug
   if (tid < nr) s_rng[tid] = kp->ranges[task.r0 + tid];
 
   // The wave's queries as the B operand of S^T = K Q^T.
-  constexpr int kQRegs = kBF ? D / 16 : D / 2;
-  using QReg = typename std::conditional<kBF, bf16x8, float>::type;
-  QReg qf[kQRegs];
+  constexpr int kQRegs = D / 2;
+  float qf[kQRegs];
 #pragma unroll
-  for (int i = 0; i < kQRegs; ++i) {
-    if constexpr (kBF)
-      qf[i] = *reinterpret_cast<const bf16x8*>(qg + qload * rs + 16 * i + 8 * g);
-    else
-      qf[i] = qg[qload * rs + 2 * i + g];
-  }
+  for (int i = 0; i < kQRegs; ++i) qf[i] = qg[qload * rs + 2 * i + g];
   __syncthreads();  // s_rng is filled
 
   // number of 64-key tiles
@@ -497,28 +502,13 @@ __device__ __forceinline__ void attn_item(KArgs kp, int32_t item, char* smem, ug
   ntiles = __builtin_amdgcn_readfirstlane(ntiles);  // uniform: it feeds scalar buffer descriptors
 
   // Per-lane LDS byte offsets.  K operand of step i: row l32 (plus 32 per
-  // block), logical chunk of dims (16i + 8g) [bf16] or element 2i + g [fp32].
+  // block), element 2i + g.
   constexpr int RB = D * int(sizeof(T));  // bytes per LDS row
   int koff[kQRegs];
 #pragma unroll
   for (int i = 0; i < kQRegs; ++i) {
-    if constexpr (kBF) {
-      const int lc = 2 * i + g;
-      koff[i] = l32 * RB + ((lc ^ Lds::k_swz(l32)) * 16);
-    } else {
-      const int e = 2 * i + g;
-      koff[i] = l32 * RB + (((e / 4) ^ Lds::k_swz(l32)) * 16) + (e % 4) * 4;
-    }
-  }
-  // V^T operand (bf16): for dim tile t, the lane's transpose-read address in
-  // 16-key chunk c, half hh is row 16c + 8hh + vrow, dims 32t + vdim .. +3.
-  const int vrow = 4 * g + ((lane & 15) >> 2);
-  const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  int voff[D / 32];
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t) {
-    const int dim = 32 * t + vdim;
-    voff[t] = vrow * RB + (((dim / 8) ^ Lds::v_swz(vrow)) * 16) + (dim % 8) * 2;
+    const int e = 2 * i + g;
+    koff[i] = l32 * RB + (((e / 4) ^ Lds::k_swz(l32)) * 16) + (e % 4) * 4;
   }
 
   f32x16 acc[D / 32];
@@ -608,79 +598,28 @@ __device__ __forceinline__ void attn_item(KArgs kp, int32_t item, char* smem, ug
       cv.advance(s_rng);
     }
 
-    if constexpr (kBF) {
-      // [A]
-      bf16x8 pb[4];
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pb[c][e] = __bf16(__builtin_amdgcn_exp2f(fmaf(s_cur[c >> 1][(c & 1) * 8 + e], c2, -m2)));
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pr = {pb[c][e], pb[c][e + 1]};
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
-        }
+      for (int j = 0; j < 16; ++j) {
+        s_cur[mb][j] = __builtin_amdgcn_exp2f(fmaf(s_cur[mb][j], c2, -m2));
+        lsum += s_cur[mb][j];
       }
-      qk_tile<T, D>(s_next, k_next, qf, koff);
+    qk_tile<T, D>(s_next, k_next, qf, koff);
 #pragma unroll
-      for (int k = 0; k < 2 * (D / 16); ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-      }
-      // [B]
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          const char* a0 = v_cur + voff[t] + (16 * c) * RB;
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * RB));
-          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[t], 0, 0, 0);
-        }
-      }
-      const float mx_next = tile_max(s_next);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);  // DS read (run ahead)
-#pragma unroll
-      for (int k = 0; k < 4 * (D / 32); ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);  // VALU
-      }
-      if (nv_next < kKT) {
-        mask_tail(s_next, nv_next);
-        update_max(tile_max(s_next), has_v);
-      } else {
-        update_max(mx_next, has_v);
-      }
-    } else {
+    for (int t = 0; t < D / 32; ++t)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          s_cur[mb][j] = __builtin_amdgcn_exp2f(fmaf(s_cur[mb][j], c2, -m2));
-          lsum += s_cur[mb][j];
+          const int key = mb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+          const int dim = 32 * t + l32;
+          const float vv = *reinterpret_cast<const float*>(v_cur + key * RB +
+                                                           (((dim / 4) ^ Lds::v_swz(key)) * 16) + (dim % 4) * 4);
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, s_cur[mb][j], acc[t], 0, 0, 0);
         }
-      qk_tile<T, D>(s_next, k_next, qf, koff);
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = mb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-            const int dim = 32 * t + l32;
-            const float vv = *reinterpret_cast<const float*>(v_cur + key * RB +
-                                                             (((dim / 4) ^ Lds::v_swz(key)) * 16) + (dim % 4) * 4);
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, s_cur[mb][j], acc[t], 0, 0, 0);
-          }
-      if (nv_next < kKT) mask_tail(s_next, nv_next);
-      update_max(tile_max(s_next), has_v);
-    }
+    if (nv_next < kKT) mask_tail(s_next, nv_next);
+    update_max(tile_max(s_next), has_v);
 
     __builtin_amdgcn_s_waitcnt(0);  // this thread's direct-to-LDS loads have landed
     __syncthreads();
@@ -706,15 +645,346 @@ __device__ __forceinline__ void attn_item(KArgs kp, int32_t item, char* smem, ug
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d0 = t * 32 + 8 * q4 + 4 * g;  // 4 consecutive dims
       char* dst = ost + l32 * RB + (((d0 / Lds::kEl16) ^ Lds::k_swz(l32)) * 16) + (d0 % Lds::kEl16) * int(sizeof(T));
-      if constexpr (kBF) {
-        bf16x4 w;
+      *reinterpret_cast<float4*>(dst) = make_float4(acc[t][4 * q4 + 0] * inv, acc[t][4 * q4 + 1] * inv,
+                                                    acc[t][4 * q4 + 2] * inv, acc[t][4 * q4 + 3] * inv);
+    }
+  // each wave reads back only its own block: LDS operations of one wave
+  // complete in order, so no barrier is needed between the write and read.
+  constexpr int rows_per_pass = 64 / Lds::kChunks;
+  constexpr int kPasses = 32 / rows_per_pass;
+  // Destination rows first, as branch-free table reads (rows past the tile
+  // are clamped for the lookup and skipped at the store), so that all the
+  // lookups are in flight together.
+  int32_t orow[kPasses];
+  if (kp->out_perm) {  // uniform
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = __bf16(acc[t][4 * q4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(dst) = w;
-      } else {
-        *reinterpret_cast<float4*>(dst) = make_float4(acc[t][4 * q4 + 0] * inv, acc[t][4 * q4 + 1] * inv,
-                                                      acc[t][4 * q4 + 2] * inv, acc[t][4 * q4 + 3] * inv);
+    for (int pass = 0; pass < kPasses; ++pass) {
+      const int32_t row = min(task.q0 + wave * 32 + pass * rows_per_pass + lane / Lds::kChunks, task.q1 - 1);
+      const bool hr = row >= kp->T && row < kp->T + kp->N;
+      const bool lr = row >= kp->T + kp->N && kp->out_lr_perm != nullptr;
+      const int32_t* tab = lr ? kp->out_lr_perm : kp->out_perm;
+      const int32_t idx = hr ? row - kp->T : lr ? row - kp->T - kp->N : 0;
+      const int32_t v = tab[idx];
+      orow[pass] = hr ? kp->T + v : lr ? kp->T + kp->N + v : row;
+    }
+  } else {
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass)
+      orow[pass] = task.q0 + wave * 32 + pass * rows_per_pass + lane / Lds::kChunks;
+  }
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int r = pass * rows_per_pass + lane / Lds::kChunks;
+    const int cc = lane % Lds::kChunks;
+    const uint4 val = *reinterpret_cast<const uint4*>(ost + r * RB + ((cc ^ Lds::k_swz(r)) * 16));
+    if (task.q0 + wave * 32 + r < task.q1)
+      *reinterpret_cast<uint4*>(og + int64_t(orow[pass]) * rs + cc * Lds::kEl16) = val;
+  }
+}
+
+
+// One bf16 query tile (plan item `item`) of the attention: the three-stage
+// pipeline described above.
+template <int D>
+__device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* smem, ug::Range* s_rng) {
+  using T = __bf16;
+  using Lds = AttnLds<T, D>;
+  constexpr int TB = Lds::kTileBytes;
+  constexpr int kQRegs = D / 16;    // k-steps of one QK^T block
+  constexpr int RB = D * 2;         // bytes per LDS row
+  constexpr int kHalfSlots = D / 8;  // QK^T MFMAs (= PV MFMAs) per tile
+  constexpr int kSlots = 2 * kHalfSlots;
+  constexpr int kExpPerSlot = 32 / kSlots;  // weights of the lane's 32 per slot
+  constexpr int kLead = 4;                  // operand reads run this many slots ahead
+  constexpr float kHeadroom = 8.0f;         // octaves between the reference and the largest weight seen
+  static_assert(kSlots * kExpPerSlot == 32, "32 weights per lane and tile");
+
+  const ug::Block blk = kp->blocks[item];
+  const ug::Task task = kp->tasks[blk.task];
+  const int32_t b = blk.bh / kp->heads, h = blk.bh - b * kp->heads;
+  const int64_t hoff = int64_t(b) * kp->batch_stride + int64_t(h) * D;
+  const T* __restrict__ qg = static_cast<const T*>(kp->q) + hoff;
+  const T* __restrict__ kg = static_cast<const T*>(kp->k) + hoff;
+  const T* __restrict__ vg = static_cast<const T*>(kp->v) + hoff;
+  T* __restrict__ og = static_cast<T*>(kp->o) + hoff;
+  const int64_t rs = kp->row_stride;
+
+  const int tid = opaque_tid<kAttnThreads>();
+  // wave index in a scalar register (the opaque tid hides that it is uniform),
+  // masked so that alias analysis keeps its range
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (kAttnWaves - 1);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int32_t qrow = task.q0 + wave * 32 + l32;
+  const int32_t qload = qrow < task.q1 ? qrow : task.q1 - 1;
+  const float c2 = kp->scale_log2;
+
+  // The task's key ranges (at most ug::kAttnMaxRanges, checked at launch)
+  // are staged in LDS, so moving to the next range inside the tile loop is an
+  // LDS read rather than a global load that would wait on the tile loads in
+  // flight.
+  const int32_t nr = task.r1 - task.r0;
+  if (tid < nr) s_rng[tid] = kp->ranges[task.r0 + tid];
+
+  // The wave's queries as the B operand of S^T = K Q^T.
+  bf16x8 qf[kQRegs];
+#pragma unroll
+  for (int i = 0; i < kQRegs; ++i) qf[i] = *reinterpret_cast<const bf16x8*>(qg + qload * rs + 16 * i + 8 * g);
+  __syncthreads();  // s_rng is filled
+
+  int32_t ntiles = 0;
+  for (int32_t r = 0; r < nr; ++r) {
+    const ug::Range rg = s_rng[r];
+    ntiles += (rg.k1 - rg.k0 + kKT - 1) / kKT;
+  }
+  ntiles = __builtin_amdgcn_readfirstlane(ntiles);  // uniform: it feeds scalar buffer descriptors
+
+  // Per-lane LDS byte offsets.  K operand of k-step i: row l32 (plus 32 per
+  // block), logical chunk of dims 16i + 8g.
+  int koff[kQRegs];
+#pragma unroll
+  for (int i = 0; i < kQRegs; ++i) {
+    const int lc = 2 * i + g;
+    koff[i] = l32 * RB + ((lc ^ Lds::k_swz(l32)) * 16);
+  }
+  // V^T operand: for dim tile t, the lane's transpose-read address in 16-key
+  // chunk c, half hh is row 16c + 8hh + vrow, dims 32t + vdim .. +3.
+  const int vrow = 4 * g + ((lane & 15) >> 2);
+  const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int voff[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    const int dim = 32 * t + vdim;
+    voff[t] = vrow * RB + (((dim / 8) ^ Lds::v_swz(vrow)) * 16) + (dim % 8) * 2;
+  }
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+  float mref;        // softmax reference, log2 units of the scaled logits
+  float lsum = 0.f;  // this lane half's share of the row sum
+
+  TileCursor ck, cv;  // next K tile to load, next V tile to load
+  ck.init(s_rng, 0, nr);
+  cv = ck;
+  TileLoader<T, D, false> kld;
+  TileLoader<T, D, true> vld;
+  kld.init(rs, tid);
+  vld.init(rs, tid);
+
+  // Scores of keys past a ragged tile's end are masked.  The empty volatile
+  // asm keeps the (rare, uniform) branch a branch.
+  auto mask_tail = [&](f32x16(&s)[2], int32_t nv) {
+    asm volatile("");
+    const int lim = nv - 4 * g;  // key 8*(j/4) + 4g + j%4 of block mb is valid iff its offset < lim
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (mb * 32 + 8 * (j >> 2) + (j & 3) >= lim) s[mb][j] = -INFINITY;
+  };
+  auto tile_max = [&](const f32x16(&s)[2]) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[mb][j]);
+    return pair_max(mx);
+  };
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  // Weight k (0..31) of the lane's scores of a tile: block k/16, register
+  // k%16; weights 2m and 2m+1 form one packed pair of P chunk m/4.  The
+  // volatile asm statements pin the work to its slot: without them the
+  // compiler gathers it after the MFMAs, where nothing hides it.
+  float e_hold = 0.f;
+  auto weight = [&](const f32x16(&s)[2], bf16x8(&p)[4], float& d, int k) {
+    const float e = __builtin_amdgcn_exp2f(fmaf(s[k >> 4][k & 15], c2, -mref));
+    if ((k & 1) == 0) {
+      e_hold = e;
+      asm volatile("" : "+v"(e_hold));
+    } else {
+      bf16x2 pr = {__bf16(e_hold), __bf16(e)};
+      asm volatile("" : "+v"(pr));
+      p[k >> 3][(k & 7) - 1] = pr[0];
+      p[k >> 3][k & 7] = pr[1];
+      // the row sum takes the rounded weights, the ones that multiply V (a
+      // dominant weight's rounding then cancels in the normalisation); a
+      // bf16 half moved into the high half of a word is that fp32 value
+      const uint32_t u = __builtin_bit_cast(uint32_t, pr);
+      d += __uint_as_float(u << 16) + __uint_as_float(u & 0xffff0000u);
+      asm volatile("" : "+v"(d));
+    }
+  };
+  auto weights_all = [&](const f32x16(&s)[2], bf16x8(&p)[4], float& d) {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) weight(s, p, d, k);
+  };
+  // Some lane's weights of tile s may be large: move the reference up by a
+  // whole number of octaves, to kHeadroom above the tile's maximum, rescale
+  // what was accumulated (exactly: a power of two) and recompute the tile's
+  // weights.  Rare and wave-uniform.
+  auto settle = [&](const f32x16(&s)[2], bf16x8(&p)[4], float& d) {
+    asm volatile("");
+    const float mt = tile_max(s) * c2;
+    const float shift = fmaxf(ceilf(mt - mref) + kHeadroom, 0.0f);
+    mref += shift;
+    const float alpha = __builtin_ldexpf(1.0f, -int(shift));
+    lsum *= alpha;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+    d = 0.f;
+    weights_all(s, p, d);
+  };
+  auto pv_all = [&](const bf16x8(&p)[4], const char* vt) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        const char* a0 = vt + voff[t] + (16 * c) * RB;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * RB));
+        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[c], acc[t], 0, 0, 0);
       }
+    }
+  };
+
+  // prologue: K_0 -> K slot 0, K_1 -> K slot 1; S_0; the reference is
+  // kHeadroom above tile 0's maximum
+  const int32_t nv0 = ck.nv();
+  kld.issue(kg, rs, ck.ks, nv0, smem, tid, wave);
+  ck.advance(s_rng);
+  int32_t nv_pend = kKT;  // rows of the K tile issued most recently (tile i+1 at the start of step i)
+  if (ntiles > 1) {
+    nv_pend = ck.nv();
+    kld.issue(kg, rs, ck.ks, nv_pend, smem + TB, tid, wave);
+    ck.advance(s_rng);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  bf16x8 pa[4], pb[4];
+  qk_tile<T, D>(sa, smem, qf, koff);
+  if (nv0 < kKT) mask_tail(sa, nv0);
+  mref = tile_max(sa) * c2 + kHeadroom;
+  __syncthreads();  // step 0 overwrites K slot 0 with K_2
+
+  // Loads of step i: K_{i+2} -> K slot i&1 (K_i was read in step i-1),
+  // V_i -> V slot i&1 (V_{i-2} was read in step i-1).
+  auto issue_loads = [&](int32_t i, int par) {
+    int32_t nv = kKT;
+    if (i + 2 < ntiles) {
+      nv = ck.nv();
+      kld.issue(kg, rs, ck.ks, nv, smem + (par ? TB : 0), tid, wave);
+      ck.advance(s_rng);
+    }
+    if (i < ntiles) {
+      vld.issue(vg, rs, cv.ks, cv.nv(), smem + 2 * TB + (par ? TB : 0), tid, wave);
+      cv.advance(s_rng);
+    }
+    return nv;
+  };
+
+  // step 0: QK^T of tile 1 || weights of tile 0 (all below 2^-kHeadroom)
+  {
+    const int32_t nv_s = nv_pend;
+    nv_pend = issue_loads(0, 0);
+    float d = 0.f;
+    weights_all(sa, pa, d);
+    if (ntiles > 1) {
+      qk_tile<T, D>(sb, smem + TB, qf, koff);
+      if (nv_s < kKT) mask_tail(sb, nv_s);
+    }
+    lsum += d;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // Step i in [1, ntiles): QK^T(i+1) || weights(i) || PV(i-1) as 2*(D/8)
+  // slots of one MFMA each (even: QK^T, odd: PV), the operand reads kLead
+  // slots ahead and 32/slots weights of tile i per slot.  The slots are
+  // fenced, so the compiler keeps this interleave.  QK^T of tile ntiles (past
+  // the end, from a stale K slot) is computed and never used.
+  auto step = [&](int32_t i, auto par, f32x16(&s_cur)[2], f32x16(&s_nxt)[2], bf16x8(&p_cur)[4],
+                  bf16x8(&p_nxt)[4]) {
+    constexpr int PAR = decltype(par)::value;                   // i & 1
+    const char* const k_next = smem + (PAR ? 0 : TB);           // K_{i+1}
+    const char* const v_prev = smem + 2 * TB + (PAR ? 0 : TB);  // V_{i-1}
+    const int32_t nv_s = nv_pend;                               // rows of tile i+1
+    const bool has_s = i + 1 < ntiles;
+    nv_pend = issue_loads(i, PAR);
+    bf16x8 opnd[kLead + 1];  // operand ring: slot k's A operand in opnd[k % (kLead + 1)]
+    auto fetch = [&](int k) {
+      const int j = k >> 1;
+      if ((k & 1) == 0) {  // QK^T: K rows of block j / kQRegs, dims of k-step j % kQRegs
+        opnd[k % (kLead + 1)] =
+            *reinterpret_cast<const bf16x8*>(k_next + (j / kQRegs) * 32 * RB + koff[j % kQRegs]);
+      } else {  // PV: V^T of 16-key chunk j / (D/32), dim tile j % (D/32)
+        const char* a0 = v_prev + voff[j % (D / 32)] + (16 * (j / (D / 32))) * RB;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * RB));
+        opnd[k % (kLead + 1)] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    };
+#pragma unroll
+    for (int k = 0; k < kLead; ++k) fetch(k);
+    float d = 0.f;
+#pragma unroll
+    for (int k = 0; k < kSlots; ++k) {
+      if (k + kLead < kSlots) fetch(k + kLead);
+      const int j = k >> 1;
+      if ((k & 1) == 0) {
+        const int mb = j / kQRegs, ks = j % kQRegs;
+        s_nxt[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[k % (kLead + 1)], qf[ks],
+                                                            ks == 0 ? f32x16{} : s_nxt[mb], 0, 0, 0);
+      } else {
+        acc[j % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[k % (kLead + 1)], p_cur[j / (D / 32)],
+                                                                    acc[j % (D / 32)], 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < kExpPerSlot; ++e) weight(s_cur, p_nxt, d, k * kExpPerSlot + e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (__builtin_amdgcn_readfirstlane(int(has_s && nv_s < kKT))) mask_tail(s_nxt, nv_s);
+    if (__ballot(!(d < 256.0f))) settle(s_cur, p_nxt, d);
+    lsum += d;
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's direct-to-LDS loads have landed
+    __syncthreads();
+  };
+
+  // Pairs of steps, so that the ring slots and register sets are fixed at
+  // compile time; the loop has no exit between the two (an exit there keeps
+  // both weight sets alive across the pair and spills).
+  int32_t i = 1;
+  for (; i + 1 < ntiles; i += 2) {
+    step(i, std::integral_constant<int, 1>{}, sb, sa, pa, pb);
+    step(i + 1, std::integral_constant<int, 0>{}, sa, sb, pb, pa);
+  }
+  if (i < ntiles) {  // one odd step left; the weights of the last tile land in pb, its V in slot 1
+    step(i, std::integral_constant<int, 1>{}, sb, sa, pa, pb);
+    pv_all(pb, smem + 3 * TB);
+  } else {  // the weights of the last tile (an even one) are in pa, its V in slot 0
+    pv_all(pa, smem + 2 * TB);
+  }
+
+  // ---- epilogue: combine the lane halves' row sums, normalise, and write
+  // the wave's 32 x D output block through LDS (swizzled rows) as full rows.
+  kp = kernel_args();  // the epilogue's arguments are loaded here, not kept across the loop
+  const float total = pair_sum(lsum);
+  const float inv = 1.0f / total;
+  if (kp->lse && g == 0 && qrow < task.q1)  // log(sum_j exp(s_j)) = (mref + log2(total)) * ln 2
+    kp->lse[int64_t(blk.bh) * kp->lse_rows + qrow] = (mref + __log2f(total)) * 0.6931471805599453f;
+  __syncthreads();  // every wave has read the last V tile before the staging below overwrites it
+  char* const ost = smem + wave * 32 * RB;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = t * 32 + 8 * q4 + 4 * g;  // 4 consecutive dims
+      char* dst = ost + l32 * RB + (((d0 / Lds::kEl16) ^ Lds::k_swz(l32)) * 16) + (d0 % Lds::kEl16) * 2;
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = __bf16(acc[t][4 * q4 + e] * inv);
+      *reinterpret_cast<bf16x4*>(dst) = w;
     }
   // each wave reads back only its own block: LDS operations of one wave
   // complete in order, so no barrier is needed between the write and read.
@@ -766,7 +1036,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
     __syncthreads();
     const int32_t item = s_item;
     if (item < 0) break;
-    attn_item<T, D>(kernel_args(), item, smem, s_rng);
+    if constexpr (std::is_same<T, __bf16>::value)
+      attn_item_bf16<D>(kernel_args(), item, smem, s_rng);
+    else
+      attn_item_f32<D>(kernel_args(), item, smem, s_rng);
     __syncthreads();  // the next item reuses the LDS and s_item
   }
   if (threadIdx.x == 0) queue_finish(kernel_args()->queue);
