@@ -19,7 +19,8 @@ UG_OK, UG_ERR_INVALID_ARGUMENT, UG_ERR_UNSUPPORTED, UG_ERR_OUT_OF_MEMORY, UG_ERR
 UG_F32, UG_BF16 = 0, 1
 UG_PLAN_HOST_ONLY = 1
 
-EXPORTED = ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr", "ug_plan_export_queues", "ug_permute",
+EXPORTED = ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr", "ug_plan_export_queues",
+            "ug_plan_export_blocks", "ug_permute",
             "ug_unpermute",
             "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_attn_fwd_lse", "ug_attn_bwd",
             "ug_rope2d_bwd", "ug_permute_rope_bwd", "ug_warm_start", "ug_status_str", "ug_last_error")
@@ -44,7 +45,8 @@ class UgInfo(ctypes.Structure):
                 ("n_neighbour_entries", c_int64), ("pairs_per_head", c_int64), ("eff_flops", c_double),
                 ("workspace_bytes", c_int64), ("attn_tasks", c_int64), ("attn_blocks", c_int64),
                 ("attn_key_tiles", c_int64), ("rope_positions", c_int64), ("bwd_workspace_bytes", c_int64),
-                ("bwd_key_tasks", c_int64), ("bwd_blocks", c_int64)]
+                ("bwd_key_tasks", c_int64), ("bwd_blocks", c_int64), ("attn_ranges", c_int64),
+                ("bwd_key_ranges", c_int64), ("bwd_mask_words", c_int64)]
 
 
 class UgError(RuntimeError):
@@ -70,6 +72,7 @@ def lib():
         L.ug_plan_export.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
         L.ug_plan_export_lr.argtypes = [c_void_p, c_void_p, c_void_p]
         L.ug_plan_export_queues.argtypes = [c_void_p, c_void_p, c_void_p]
+        L.ug_plan_export_blocks.argtypes = [c_void_p] * 7
         L.ug_permute.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
         L.ug_unpermute.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
         L.ug_rope2d.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
@@ -86,7 +89,7 @@ def lib():
         L.ug_last_error.argtypes = []
         L.ug_last_error.restype = c_char_p
         for name in ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr",
-                     "ug_plan_export_queues", "ug_permute",
+                     "ug_plan_export_queues", "ug_plan_export_blocks", "ug_permute",
                      "ug_unpermute",
                      "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_attn_fwd_lse",
                      "ug_attn_bwd", "ug_rope2d_bwd", "ug_permute_rope_bwd", "ug_warm_start"):
@@ -199,6 +202,25 @@ def ug_plan_export_lr(plan: Plan) -> dict:
     lr_win_off = np.empty(info["n_windows"] + 2, np.int32)
     _check("ug_plan_export_lr", lib().ug_plan_export_lr(plan.handle, lr_perm.ctypes.data, lr_win_off.ctypes.data))
     return {"lr_perm": lr_perm[:info["n_lr"]], "lr_win_off": lr_win_off}
+
+
+def ug_plan_export_blocks(plan: Plan) -> dict:
+    """The block lists the attention kernels walk: query tiles [n, 4] (q0, q1,
+    r0, r1) with key ranges [m, 2] (k0, k1), and the backward's key tiles with
+    their query ranges and per-key 64-bit range masks (mask_off -1: unmasked)."""
+    info = plan.info
+    q_tiles = np.empty((max(1, info["attn_tasks"]), 4), np.int32)
+    k_ranges = np.empty((max(1, info["attn_ranges"]), 2), np.int32)
+    k_tiles = np.empty((max(1, info["bwd_key_tasks"]), 4), np.int32)
+    q_ranges = np.empty((max(1, info["bwd_key_ranges"]), 2), np.int32)
+    mask_off = np.empty(max(1, info["bwd_key_tasks"]), np.int32)
+    masks = np.empty(max(1, info["bwd_mask_words"]), np.uint64)
+    _check("ug_plan_export_blocks", lib().ug_plan_export_blocks(
+        plan.handle, q_tiles.ctypes.data, k_ranges.ctypes.data, k_tiles.ctypes.data, q_ranges.ctypes.data,
+        mask_off.ctypes.data, masks.ctypes.data))
+    return {"q_tiles": q_tiles[:info["attn_tasks"]], "k_ranges": k_ranges[:info["attn_ranges"]],
+            "k_tiles": k_tiles[:info["bwd_key_tasks"]], "q_ranges": q_ranges[:info["bwd_key_ranges"]],
+            "mask_off": mask_off[:info["bwd_key_tasks"]], "masks": masks[:info["bwd_mask_words"]]}
 
 
 # ---------------------------------------------------------------- device calls

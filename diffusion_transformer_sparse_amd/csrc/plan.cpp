@@ -639,6 +639,9 @@ ug_status ug_plan_info(ug_plan_t p, ug_info* out) {
   out->bwd_workspace_bytes = p->bwd_workspace_bytes();
   out->bwd_key_tasks = int64_t(p->ktasks.size());
   out->bwd_blocks = int64_t(p->kblocks.size());
+  out->attn_ranges = int64_t(p->ranges.size());
+  out->bwd_key_ranges = int64_t(p->kranges.size());
+  out->bwd_mask_words = int64_t(p->kmasks.size());
   return UG_OK;
 }
 
@@ -671,6 +674,34 @@ ug_status ug_plan_export_queues(ug_plan_t p, int32_t* attn_items, int32_t* bwd_i
   };
   if (attn_items) put(p->blocks, attn_items);
   if (bwd_items) put(p->kblocks, bwd_items);
+  return UG_OK;
+}
+
+ug_status ug_plan_export_blocks(ug_plan_t p, int32_t* q_tiles, int32_t* k_ranges, int32_t* k_tiles,
+                                int32_t* q_ranges, int32_t* mask_off, uint64_t* masks) {
+  ug::clear_error();
+  if (!p) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_plan_export_blocks: plan is NULL");
+  auto put_tasks = [](const std::vector<ug::Task>& t, int32_t* out) {
+    for (size_t i = 0; i < t.size(); ++i) {
+      out[4 * i] = t[i].q0;
+      out[4 * i + 1] = t[i].q1;
+      out[4 * i + 2] = t[i].r0;
+      out[4 * i + 3] = t[i].r1;
+    }
+  };
+  auto put_ranges = [](const std::vector<ug::Range>& r, int32_t* out) {
+    for (size_t i = 0; i < r.size(); ++i) {
+      out[2 * i] = r[i].k0;
+      out[2 * i + 1] = r[i].k1;
+    }
+  };
+  if (q_tiles) put_tasks(p->tasks, q_tiles);
+  if (k_ranges) put_ranges(p->ranges, k_ranges);
+  if (k_tiles) put_tasks(p->ktasks, k_tiles);
+  if (q_ranges) put_ranges(p->kranges, q_ranges);
+  if (mask_off && !p->kmask_off.empty())
+    std::memcpy(mask_off, p->kmask_off.data(), p->kmask_off.size() * sizeof(int32_t));
+  if (masks && !p->kmasks.empty()) std::memcpy(masks, p->kmasks.data(), p->kmasks.size() * sizeof(uint64_t));
   return UG_OK;
 }
 

@@ -122,6 +122,9 @@ typedef struct ug_info {
   int64_t bwd_workspace_bytes; /* bytes ug_attn_bwd needs as workspace */
   int64_t bwd_key_tasks;       /* key tiles per (batch, head) of the dK/dV pass */
   int64_t bwd_blocks;          /* workgroups one dK/dV pass launches */
+  int64_t attn_ranges;         /* key ranges of all query tiles (ug_plan_export_blocks) */
+  int64_t bwd_key_ranges;      /* query ranges of all key tiles */
+  int64_t bwd_mask_words;      /* 64-bit range masks of the masked key tiles */
 } ug_info;
 
 typedef struct ug_plan_s* ug_plan_t;
@@ -175,6 +178,38 @@ ug_status ug_plan_export_lr(ug_plan_t plan, int32_t* lr_perm, int32_t* lr_win_of
  * on (a cursor on padding means that queue is empty).
  */
 ug_status ug_plan_export_queues(ug_plan_t plan, int32_t* attn_items, int32_t* bwd_items);
+
+/*
+ * ug_plan_export_blocks: the block lists the attention kernels walk, for
+ * bit-exact tests of the mask they encode (关键设计 1-2: windows, adjacent
+ * windows, text and LR anchors).  Any pointer may be NULL to skip a table.
+ * Rows are rows of the permuted sequence; every list is per (batch, head)
+ * and the same for all of them.
+ *  q_tiles    int32[4 * info.attn_tasks]   query tile t: query rows
+ *                                          [q_tiles[4t], q_tiles[4t+1]) see
+ *                                          the key ranges q_tiles[4t+2] ..
+ *                                          q_tiles[4t+3]-1 of k_ranges
+ *  k_ranges   int32[2 * info.attn_ranges]  range r: key rows [k_ranges[2r],
+ *                                          k_ranges[2r+1])
+ *  k_tiles    int32[4 * info.bwd_key_tasks] key tile u of the backward's
+ *                                          dK/dV pass: key rows [k_tiles[4u],
+ *                                          k_tiles[4u+1]) and the query ranges
+ *                                          k_tiles[4u+2] .. k_tiles[4u+3]-1
+ *                                          of q_ranges
+ *  q_ranges   int32[2 * info.bwd_key_ranges] range r: query rows
+ *                                          [q_ranges[2r], q_ranges[2r+1])
+ *  mask_off   int32[info.bwd_key_tasks]    -1: every key of tile u sees all
+ *                                          of the tile's query ranges; else
+ *                                          key row k_tiles[4u] + j sees its
+ *                                          tile's range number b iff bit b of
+ *                                          masks[mask_off[u] + j] is set
+ *  masks      uint64[info.bwd_mask_words]
+ * The union of a query row's ranges is exactly the set of keys it attends
+ * to, and the union of a key row's (masked) ranges exactly the queries that
+ * attend to it.
+ */
+ug_status ug_plan_export_blocks(ug_plan_t plan, int32_t* q_tiles, int32_t* k_ranges, int32_t* k_tiles,
+                                int32_t* q_ranges, int32_t* mask_off, uint64_t* masks);
 
 /*
  * ug_permute: x_perm = x_raster with HR rows gathered into window-first
