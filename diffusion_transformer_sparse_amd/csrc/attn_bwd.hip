@@ -576,8 +576,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
 }
 
 template <int D>
-void launch_bwd(ug_plan_t p, BwdParams bp, const __bf16* o, const float* lse, float* lse2, float* delta,
-                hipStream_t s) {
+ug_status launch_bwd(ug_plan_t p, BwdParams bp, const __bf16* o, const float* lse, float* lse2, float* delta,
+                     hipStream_t s, const char* fn) {
   const int32_t Lp = int32_t(p->stat_rows());
   const int32_t units = std::min(p->d.heads, kPrepHeads) * (D / 8);
   const unsigned prep_threads = unsigned(std::min(1024, (units + 63) / 64 * 64));
@@ -589,10 +589,14 @@ void launch_bwd(ug_plan_t p, BwdParams bp, const __bf16* o, const float* lse, fl
   bp.ranges = p->d_ranges;
   bp.blocks = p->d_blocks;
   if (!p->blocks.empty()) {
-    bp.queue = p->next_queue_slot();
     bp.queue_len = int32_t(p->blocks.size() / ug::kXcds);
     const unsigned grid = unsigned(std::min<size_t>(size_t(p->cus), p->blocks.size()));
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3(grid), dim3(kThreads), 0, s, bp);
+    const ug_status st = ug::launch_with_slot(p, s, fn, [&](int32_t* cursors) {
+      bp.queue = cursors;
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3(grid), dim3(kThreads), 0, s, bp);
+      return launch_status(fn);
+    });
+    if (st != UG_OK) return st;
   }
   bp.tasks = p->d_ktasks;
   bp.ranges = p->d_kranges;
@@ -601,6 +605,7 @@ void launch_bwd(ug_plan_t p, BwdParams bp, const __bf16* o, const float* lse, fl
   bp.masks = p->d_kmasks;
   if (!p->kblocks.empty())
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3(unsigned(p->kblocks.size())), dim3(kThreads), 0, s, bp);
+  return launch_status(fn);
 }
 
 }  // namespace
@@ -672,11 +677,8 @@ ug_status ug_attn_bwd(ug_plan_t p, const void* q, const void* k, const void* v, 
   bp.scale_log2 = float(1.4426950408889634 / std::sqrt(double(p->d.head_dim)));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const __bf16* ob = static_cast<const __bf16*>(o);
-  if (p->d.head_dim == 128)
-    launch_bwd<128>(p, bp, ob, lse, lse2, delta, s);
-  else
-    launch_bwd<64>(p, bp, ob, lse, lse2, delta, s);
-  return launch_status(fn);
+  if (p->d.head_dim == 128) return launch_bwd<128>(p, bp, ob, lse, lse2, delta, s, fn);
+  return launch_bwd<64>(p, bp, ob, lse, lse2, delta, s, fn);
 }
 
 }  // extern "C"

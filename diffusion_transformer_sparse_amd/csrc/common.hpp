@@ -126,10 +126,12 @@ __device__ __forceinline__ int32_t queue_grab(int32_t* queue, int32_t queue_len,
   return -1;
 }
 // Once per workgroup, after its last (failed) grab: the last workgroup to
-// finish clears the slot for a later launch.  Every other workgroup has made
-// its last grab before counting itself finished, so no cursor moves after.
+// finish clears the slot for a later launch.  The finish count is acq_rel:
+// each workgroup's grabs happen before its release, and the last one's
+// acquire orders every workgroup's grabs before its clearing stores, so no
+// cursor moves after it is cleared.
 __device__ __forceinline__ void queue_finish(int32_t* queue) {
-  if (__hip_atomic_fetch_add(queue + ug::kXcds, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+  if (__hip_atomic_fetch_add(queue + ug::kXcds, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
       int32_t(gridDim.x * gridDim.y * gridDim.z) - 1)
     for (int x = 0; x <= ug::kXcds; ++x) __hip_atomic_store(queue + x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -1117,19 +1117,21 @@ ug_status attn_common(ug_plan_t p, const void* q, const void* k, const void* v, 
   ap.out_lr_perm = raster_out ? p->d_lr_perm : nullptr;
   ap.lse = lse;
   ap.lse_rows = p->L;
-  ap.queue = p->next_queue_slot();
   ap.queue_len = int32_t(p->blocks.size() / ug::kXcds);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = p->d.dtype == UG_BF16;
-  if (bf && p->d.head_dim == 128)
-    launch_attn<__bf16, 128>(p, ap, s);
-  else if (bf && p->d.head_dim == 64)
-    launch_attn<__bf16, 64>(p, ap, s);
-  else if (!bf && p->d.head_dim == 128)
-    launch_attn<float, 128>(p, ap, s);
-  else
-    launch_attn<float, 64>(p, ap, s);
-  return launch_status(fn);
+  return ug::launch_with_slot(p, s, fn, [&](int32_t* cursors) {
+    ap.queue = cursors;
+    if (bf && p->d.head_dim == 128)
+      launch_attn<__bf16, 128>(p, ap, s);
+    else if (bf && p->d.head_dim == 64)
+      launch_attn<__bf16, 64>(p, ap, s);
+    else if (!bf && p->d.head_dim == 128)
+      launch_attn<float, 128>(p, ap, s);
+    else
+      launch_attn<float, 64>(p, ap, s);
+    return launch_status(fn);
+  });
 }
 
 template <bool kInverse>

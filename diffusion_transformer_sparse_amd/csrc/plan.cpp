@@ -499,6 +499,10 @@ void free_device(ug_plan_s* p) {
                   p->d_kblocks, p->d_kmasks, p->d_kmask_off, p->d_queue};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
+  for (hipEvent_t& e : p->slot_events) {
+    if (e) (void)hipEventDestroy(e);
+    e = nullptr;
+  }
   p->d_perm = p->d_inv = nullptr;
   p->d_lr_perm = p->d_lr_inv = nullptr;
   p->d_rope = nullptr;
@@ -543,6 +547,12 @@ ug_status alloc_queue(ug_plan_s* p) {
   if (hipMemset(p->d_queue, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
     return fail(UG_ERR_HIP, std::string("ug_plan: clearing the work-queue cursors failed: ") +
                                 hipGetErrorString(hipGetLastError()));
+  for (hipEvent_t& e : p->slot_events)
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+      e = nullptr;
+      return fail(UG_ERR_HIP, std::string("ug_plan: hipEventCreateWithFlags failed: ") +
+                                  hipGetErrorString(hipGetLastError()));
+    }
   return UG_OK;
 }
 

@@ -2,12 +2,15 @@
 // kernel launchers (kernels.hip).  Not part of the public ABI.
 #pragma once
 
-#include <atomic>
+#include <hip/hip_runtime_api.h>
+
 #include <cstdint>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "../../include/ultragen.h"
+#include "slot_ring.hpp"
 
 namespace ug {
 
@@ -35,7 +38,9 @@ constexpr int kAttnMaxRanges = 64;   // key ranges one query tile may have (stag
 // Work-queue cursors of the persistent attention grid: each launch takes one
 // slot of kQueueSlotInts int32 (one cursor per XCD queue, then the count of
 // workgroups that have finished), round-robin over kQueueSlots slots, so that
-// launches with one plan that run at the same time use different cursors.
+// launches with one plan that run at the same time use different cursors; a
+// launch that gets a slot back waits for the slot's previous launch (an event
+// per slot), so two launches never share cursors.
 constexpr int kQueueSlots = 64;
 constexpr int kQueueSlotInts = 16;
 
@@ -97,17 +102,44 @@ struct ug_plan_s {
   uint64_t* d_kmasks = nullptr;  // null when no key tile is masked
 
   // Persistent attention grid: one workgroup per compute unit, and the
-  // zeroed work-queue cursor slots (each launch leaves its slot at zero).
+  // zeroed work-queue cursor slots (each launch leaves its slot at zero),
+  // handed out by `slots` under `launch_mu`, with the event recorded after
+  // each slot's latest launch.
   int32_t cus = 0;
   int32_t* d_queue = nullptr;
-  std::atomic<uint32_t> launches{0};
-  int32_t* next_queue_slot() {
-    return d_queue + size_t(launches.fetch_add(1, std::memory_order_relaxed) % ug::kQueueSlots) * ug::kQueueSlotInts;
-  }
+  std::mutex launch_mu;
+  ug::SlotRing<ug::kQueueSlots> slots;
+  hipEvent_t slot_events[ug::kQueueSlots] = {};
 };
 
 namespace ug {
 // thread-local last-error message helpers (plan.cpp)
 ug_status fail(ug_status s, const std::string& msg);
 void clear_error();
+
+// Launch of a persistent grid with one of the plan's cursor slots: refuses
+// stream capture (a captured launch would take its slot at capture time and
+// share it with every replay), takes the next slot, makes the stream wait
+// for the slot's previous launch, runs `launch(cursors)` and records the
+// slot's event after it.  Returns UG_OK or a failure already reported.
+template <typename F>
+ug_status launch_with_slot(ug_plan_s* p, hipStream_t s, const char* fn, F&& launch) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(UG_ERR_HIP, std::string(fn) + ": hipStreamIsCapturing failed");
+  }
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(UG_ERR_UNSUPPORTED, std::string(fn) + ": stream capture is not supported (each launch takes a "
+                                                      "work-queue cursor slot at launch time)");
+  std::lock_guard<std::mutex> lock(p->launch_mu);
+  const auto t = p->slots.take();
+  if (t.reused && hipStreamWaitEvent(s, p->slot_events[t.slot], 0) != hipSuccess)
+    return fail(UG_ERR_HIP, std::string(fn) + ": hipStreamWaitEvent failed: " + hipGetErrorString(hipGetLastError()));
+  const ug_status st = launch(p->d_queue + size_t(t.slot) * kQueueSlotInts);
+  if (st != UG_OK) return st;
+  if (hipEventRecord(p->slot_events[t.slot], s) != hipSuccess)
+    return fail(UG_ERR_HIP, std::string(fn) + ": hipEventRecord failed: " + hipGetErrorString(hipGetLastError()));
+  return UG_OK;
+}
 }  // namespace ug

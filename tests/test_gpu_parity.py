@@ -289,6 +289,48 @@ def test_attention_queue_cursors_reused_and_concurrent(U):
     assert torch.equal(bits(o1), bits(ref)) and torch.equal(bits(o2), bits(ref2))
 
 
+@pytest.mark.gpu
+def test_attention_cursor_slots_wrap_while_in_flight(U):
+    """130 launches with one plan alternate between two streams with no
+    synchronisation, so every cursor slot comes back while its previous
+    launch may still run on the other stream; the launcher makes the new
+    launch wait for that one, so every output matches the serial result."""
+    import torch
+    w = WL.WORKLOADS["small_ragged"]
+    p = plan_of(U, w)
+    q, k, v = qkv_device(w)
+    ref = U.ug_attn_fwd(p, q, k, v)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(ref) for _ in range(130)]
+    for j, out in enumerate(outs):
+        with torch.cuda.stream(streams[j % 2]):
+            U.ug_attn_fwd(p, q, k, v, out)
+    torch.cuda.synchronize()
+    for j, out in enumerate(outs):
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"launch {j}"
+
+
+@pytest.mark.gpu
+def test_attention_refuses_stream_capture(U):
+    """A captured launch would take its cursor slot once, at capture time,
+    and share it with every replay: the persistent launches refuse capture
+    (before launching anything) with UG_ERR_UNSUPPORTED."""
+    import torch
+    w = WL.WORKLOADS["tiny"]
+    p = plan_of(U, w)
+    q, k, v = qkv_device(w)
+    o = torch.empty_like(q)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(U.UgError) as err:
+        with torch.cuda.graph(g):
+            U.ug_attn_fwd(p, q, k, v, o)
+    assert err.value.status == 2  # UG_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.isfinite(U.ug_attn_fwd(p, q, k, v)).all()  # the plan still works afterwards
+
+
 # ------------------------------------------------------------------ edge cases
 
 EDGE = {
