@@ -23,6 +23,7 @@ EXPORTED = ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_pla
             "ug_plan_export_blocks", "ug_permute",
             "ug_unpermute",
             "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_attn_fwd_lse", "ug_attn_bwd",
+            "ug_attn_bwd_noalloc",
             "ug_rope2d_bwd", "ug_permute_rope_bwd", "ug_warm_start", "ug_status_str", "ug_last_error")
 
 
@@ -81,6 +82,7 @@ def lib():
         L.ug_permute_rope.argtypes = [c_void_p] * 6
         L.ug_attn_fwd_lse.argtypes = [c_void_p] * 8
         L.ug_attn_bwd.argtypes = [c_void_p] * 12
+        L.ug_attn_bwd_noalloc.argtypes = [c_void_p] * 11
         L.ug_rope2d_bwd.argtypes = [c_void_p] * 4
         L.ug_permute_rope_bwd.argtypes = [c_void_p] * 6
         L.ug_warm_start.argtypes = [POINTER(UgWarmDesc), c_void_p, c_void_p, c_void_p, c_void_p]
@@ -92,7 +94,7 @@ def lib():
                      "ug_plan_export_queues", "ug_plan_export_blocks", "ug_permute",
                      "ug_unpermute",
                      "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_attn_fwd_lse",
-                     "ug_attn_bwd", "ug_rope2d_bwd", "ug_permute_rope_bwd", "ug_warm_start"):
+                     "ug_attn_bwd", "ug_attn_bwd_noalloc", "ug_rope2d_bwd", "ug_permute_rope_bwd", "ug_warm_start"):
             getattr(L, name).restype = c_int32
         _lib = L
     return _lib
@@ -358,6 +360,17 @@ def ug_attn_bwd(plan: Plan, q, k, v, o, d_o, lse, dq=None, dk=None, dv=None, wor
     vp = lambda t: c_void_p(t.data_ptr())
     _check("ug_attn_bwd", lib().ug_attn_bwd(plan.handle, vp(q), vp(k), vp(v), vp(o), vp(d_o), vp(lse), vp(dq), vp(dk),
                                             vp(dv), vp(workspace), _stream_ptr(q)))
+    return dq, dk, dv
+
+
+def ug_attn_bwd_noalloc(plan: Plan, q, k, v, o, d_o, lse, dq, dk, dv):
+    """ug_attn_bwd with the statistics in the library's per-GPU scratch: the
+    caller passes inputs and outputs only, nothing is allocated."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_tensor(plan, t, n)
+    vp = lambda t: c_void_p(t.data_ptr())
+    _check("ug_attn_bwd_noalloc", lib().ug_attn_bwd_noalloc(plan.handle, vp(q), vp(k), vp(v), vp(o), vp(d_o),
+                                                            vp(lse), vp(dq), vp(dk), vp(dv), _stream_ptr(q)))
     return dq, dk, dv
 
 

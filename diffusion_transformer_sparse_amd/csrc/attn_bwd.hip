@@ -24,6 +24,8 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
+#include <string>
 
 namespace {
 
@@ -608,53 +610,87 @@ ug_status launch_bwd(ug_plan_t p, BwdParams bp, const __bf16* o, const float* ls
   return launch_status(fn);
 }
 
-}  // namespace
+// Scratch of ug_attn_bwd_noalloc: the per-row statistics (log2 LSE and
+// Delta) that ug_attn_bwd keeps in the caller's workspace.  One copy per
+// GPU, for the life of the process; host code uses the address that
+// hipGetSymbolAddress returns for the current device, never the array's name.
+constexpr size_t kBwdScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kBwdScratchBytes];
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kScratchDevices] = {};
 
-extern "C" {
+// The scratch address on `device` (which must be current), looked up once.
+ug_status scratch_on(int device, void** out) {
+  if (device < 0 || device >= kScratchDevices)
+    return ug::fail(UG_ERR_UNSUPPORTED, "ug_attn_bwd_noalloc: device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[device]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return ug::fail(UG_ERR_HIP, std::string("ug_attn_bwd_noalloc: hipGetSymbolAddress of the scratch failed: ") +
+                                      hipGetErrorString(e));
+    }
+    g_scratch[device] = ptr;
+  }
+  *out = g_scratch[device];
+  return UG_OK;
+}
 
-ug_status ug_attn_bwd(ug_plan_t p, const void* q, const void* k, const void* v, const void* o, const void* d_o,
-                      const float* lse, void* dq, void* dk, void* dv, void* workspace, void* stream) {
-  const char* fn = "ug_attn_bwd";
-  ug::clear_error();
+// The backward with its statistics in `workspace`, or (use_scratch) in the
+// device's scratch, looked up once every argument has been checked.
+ug_status bwd_common(ug_plan_t p, const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                     const float* lse, void* dq, void* dk, void* dv, void* workspace, bool use_scratch, void* stream,
+                     const char* fn) {
   ug_status st = check_plan(p, fn);
   if (st != UG_OK) return st;
-  if (p->d.dtype != UG_BF16) return ug::fail(UG_ERR_UNSUPPORTED, "ug_attn_bwd: only bf16 plans are supported");
+  if (p->d.dtype != UG_BF16) return ug::fail(UG_ERR_UNSUPPORTED, std::string(fn) + ": only bf16 plans are supported");
   if (p->d.head_dim != 64 && p->d.head_dim != 128)
-    return ug::fail(UG_ERR_UNSUPPORTED, "ug_attn_bwd: head_dim must be 64 or 128");
+    return ug::fail(UG_ERR_UNSUPPORTED, std::string(fn) + ": head_dim must be 64 or 128");
   const void* ins[] = {q, k, v, o, d_o};
   void* outs[] = {dq, dk, dv};
   for (const void* x : ins)
-    if (!x || !aligned16(x)) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: NULL or unaligned input tensor");
+    if (!x || !aligned16(x)) return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": NULL or unaligned input tensor");
   for (const void* x : outs)
-    if (!x || !aligned16(x)) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: NULL or unaligned output tensor");
+    if (!x || !aligned16(x)) return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": NULL or unaligned output tensor");
   if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u))
-    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: NULL or unaligned lse");
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": NULL or unaligned lse");
   const int64_t ws_bytes = p->bwd_workspace_bytes();
-  if (!workspace || !aligned16(workspace))
-    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: workspace must be a 16-byte aligned buffer of "
+  if (use_scratch && ws_bytes > int64_t(kBwdScratchBytes))
+    return ug::fail(UG_ERR_UNSUPPORTED, std::string(fn) + ": the plan needs " + std::to_string(ws_bytes) +
+                                            " bytes of statistics, more than the " +
+                                            std::to_string(kBwdScratchBytes) + "-byte scratch; use ug_attn_bwd");
+  if (!use_scratch && (!workspace || !aligned16(workspace)))
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": workspace must be a 16-byte aligned buffer of "
                                              "info.bwd_workspace_bytes bytes");
   const int64_t n = tensor_bytes(p);
   const int64_t nl = int64_t(p->d.batch) * p->d.heads * p->L * int64_t(sizeof(float));
   for (int a = 0; a < 3; ++a) {
     for (int c = a + 1; c < 3; ++c)
       if (overlap_ranges(outs[a], n, outs[c], n))
-        return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: dq, dk and dv must not overlap");
+        return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": dq, dk and dv must not overlap");
     for (const void* x : ins)
       if (overlap_ranges(outs[a], n, x, n))
-        return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: an output overlaps an input");
+        return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": an output overlaps an input");
     if (overlap_ranges(outs[a], n, lse, nl) || overlap_ranges(outs[a], n, workspace, ws_bytes))
-      return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: an output overlaps lse or the workspace");
+      return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": an output overlaps lse or the workspace");
   }
   for (const void* x : ins)
     if (overlap_ranges(workspace, ws_bytes, x, n))
-      return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: the workspace overlaps an input");
+      return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": the workspace overlaps an input");
   if (overlap_ranges(workspace, ws_bytes, lse, nl))
-    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: the workspace overlaps lse");
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": the workspace overlaps lse");
   if (p->max_task_ranges > ug::kAttnMaxRanges || p->kmax_task_ranges > ug::kAttnMaxRanges)
-    return ug::fail(UG_ERR_UNSUPPORTED, "ug_attn_bwd: a tile has more row ranges than the kernels stage (" +
+    return ug::fail(UG_ERR_UNSUPPORTED, std::string(fn) + ": a tile has more row ranges than the kernels stage (" +
                                             std::to_string(ug::kAttnMaxRanges) + "); use a smaller radius");
   if (current_device() != p->device)
-    return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_attn_bwd: current device is not the plan's device");
+    return ug::fail(UG_ERR_INVALID_ARGUMENT, std::string(fn) + ": current device is not the plan's device");
+  if (use_scratch) {  // a static region: it cannot overlap the caller's buffers
+    st = scratch_on(p->device, &workspace);
+    if (st != UG_OK) return st;
+  }
 
   BwdParams bp{};
   bp.q = static_cast<const __bf16*>(q);
@@ -679,6 +715,22 @@ ug_status ug_attn_bwd(ug_plan_t p, const void* q, const void* k, const void* v, 
   const __bf16* ob = static_cast<const __bf16*>(o);
   if (p->d.head_dim == 128) return launch_bwd<128>(p, bp, ob, lse, lse2, delta, s, fn);
   return launch_bwd<64>(p, bp, ob, lse, lse2, delta, s, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+ug_status ug_attn_bwd(ug_plan_t p, const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                      const float* lse, void* dq, void* dk, void* dv, void* workspace, void* stream) {
+  ug::clear_error();
+  return bwd_common(p, q, k, v, o, d_o, lse, dq, dk, dv, workspace, false, stream, "ug_attn_bwd");
+}
+
+ug_status ug_attn_bwd_noalloc(ug_plan_t p, const void* q, const void* k, const void* v, const void* o,
+                              const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* stream) {
+  ug::clear_error();
+  return bwd_common(p, q, k, v, o, d_o, lse, dq, dk, dv, nullptr, true, stream, "ug_attn_bwd_noalloc");
 }
 
 }  // extern "C"

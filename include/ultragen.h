@@ -310,6 +310,25 @@ ug_status ug_attn_bwd(ug_plan_t plan, const void* q, const void* k, const void* 
                       const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* workspace,
                       void* stream);
 ug_status ug_rope2d_bwd(ug_plan_t plan, void* dq_perm, void* dk_perm, void* stream);
+
+/*
+ * ug_attn_bwd_noalloc: ug_attn_bwd for callers that cannot allocate device
+ * memory (tight serving or training loops, harnesses that forbid hipMalloc):
+ * the same kernels and results, with the per-row statistics kept in a
+ * library-owned scratch array instead of a caller workspace.  It calls no
+ * allocating routine.
+ *  - The scratch is 64 MiB (67108864 bytes) per GPU, held from the first
+ *    call on that GPU until the process ends; a plan whose
+ *    info.bwd_workspace_bytes exceeds it gets UG_ERR_UNSUPPORTED (use
+ *    ug_attn_bwd).  4K with 24 heads needs 13.5 MB, 8K 53.6 MB.
+ *  - Every call on one GPU uses that GPU's one scratch: calls that overlap in
+ *    time on one GPU (other streams, other threads, other plans) race and
+ *    must be serialised by the caller.  Nothing in it needs clearing: each
+ *    call writes every statistic it reads.
+ *  - Same arguments and rules as ug_attn_bwd otherwise.
+ */
+ug_status ug_attn_bwd_noalloc(ug_plan_t plan, const void* q, const void* k, const void* v, const void* o,
+                              const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* stream);
 ug_status ug_permute_rope_bwd(ug_plan_t plan, const void* dq_perm, const void* dk_perm, void* dq_raster,
                               void* dk_raster, void* stream);
 
