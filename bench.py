@@ -65,30 +65,66 @@ def measured_traffic(workload: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float):
-    """The fp64 oracle (as it stands) on a bounded sample: whole heads of the
-    same workload, RoPE + grouped composite attention, until `budget_s`."""
-    import numpy as np
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+_POOL_BARRIER = None
+
+
+def _pool_init(barrier):
+    global _POOL_BARRIER
+    _POOL_BARRIER = barrier
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)  # one BLAS thread per process: the processes use the cores
+    except Exception:
+        pass
+
+
+def _oracle_head(args):
+    """One head of the oracle in a worker: inputs first, then every worker
+    starts the oracle call together (barrier) and times it."""
     import workloads as WL
     from oracle import ultragen_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    name, h = args
+    w = WL.WORKLOADS[name]
     geo = O.geometry_of(w)
-    per_head_flops = 4.0 * w.head_dim * O.pair_count(geo)
-    heads, elapsed = 0, 0.0
-    while heads < w.heads and elapsed < budget_s:
-        q, k, v = (WL.head_f64(w, t, heads) for t in (WL.Q, WL.K, WL.V))
-        t0 = time.perf_counter()           # time the oracle call only, not input generation
-        O.forward_head(geo, q, k, v, w.rope_theta)
-        elapsed += time.perf_counter() - t0
-        heads += 1
-    return {"value": per_head_flops * heads / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle", "sample": f"{heads} of {w.heads} heads of the {w.name} layer "
-                                        f"(fp64 numpy RoPE + grouped masked attention; input generation not timed)",
-            "seconds": round(elapsed, 2)}
+    q, k, v = (WL.head_f64(w, t, h) for t in (WL.Q, WL.K, WL.V))
+    _POOL_BARRIER.wait()
+    t0 = time.perf_counter()  # CLOCK_MONOTONIC: comparable across the processes
+    O.forward_head(geo, q, k, v, w.rope_theta)
+    return t0, time.perf_counter()
+
+
+def cpu_baseline(w, max_procs: int):
+    """The fp64 oracle (as it stands) on a bounded sample of the same layer:
+    whole heads, one per process, on up to `max_procs` host cores at once (one
+    BLAS thread each), all started together; the rate is the sample's
+    effective FLOP over the wall time from the first start to the last end.
+    Runs before the GPU is touched (the workers are forked)."""
+    import multiprocessing as mp
+    from oracle import ultragen_oracle as O
+    nproc = os.cpu_count() or 1
+    procs = max(1, min(nproc, max_procs, w.heads))
+    ctx = mp.get_context("fork")
+    barrier = ctx.Barrier(procs)
+    with ctx.Pool(procs, initializer=_pool_init, initargs=(barrier,)) as pool:
+        spans = pool.map(_oracle_head, [(w.name, h) for h in range(procs)], chunksize=1)
+    wall = max(e for _, e in spans) - min(s0 for s0, _ in spans)
+    per_head_flops = 4.0 * w.head_dim * O.pair_count(O.geometry_of(w))
+    return {"value": per_head_flops * procs / wall / 1e12, "unit": "TFLOP/s", "cores": procs, "kind": "oracle",
+            "sample": f"{procs} of {w.heads} heads of the {w.name} layer, one per process, 1 BLAS thread each, "
+                      f"started together (fp64 numpy RoPE + grouped masked attention; input generation not timed)",
+            "seconds": round(wall, 2), "nproc": nproc, "cpu_model": _cpu_model(), "processes": procs,
+            "blas_threads_per_process": 1}
 
 
 def main():
@@ -97,7 +133,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="4k")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--cpu-procs", type=int, default=16,
+                    help="most host processes for cpu_baseline (the host's CPU share per GPU)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward step measurement")
     ap.add_argument("--no-warm", action="store_true", help="skip the warm-start kernel measurement")
@@ -108,11 +145,15 @@ def main():
         sys.exit(2)
 
     import numpy as np
-    import torch
     import workloads as WL
-    import diffusion_transformer_sparse_amd as U
 
     w = WL.WORKLOADS[args.workload]
+    # the CPU baseline first, in forked worker processes, before anything touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_procs)
+
+    import torch
+    import diffusion_transformer_sparse_amd as U
+
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_plan = time.perf_counter()
@@ -297,8 +338,8 @@ def main():
         "plan_build_s": round(t_plan, 4),
         "kernel_sha": kernel_hash(),
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 
