@@ -251,6 +251,20 @@ def test_backward_is_deterministic(U):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+def test_full_size_backward_whole_head(U):
+    """The 4K layer's backward: dq, dk and dv of every row of one head
+    (text, HR and LR queries and keys) against the oracle's whole-head
+    backward."""
+    w = WL.WORKLOADS["4k"]
+    p, (_, dq_d, dk_d, dv_d) = run_layer_bwd(U, w, host=False)
+    h = 9
+    got = [to_host_f64(t[0, :, h].contiguous(), w.dtype) for t in (dq_d, dk_d, dv_d)]
+    for _, geo, (qh, kh, vh, doh) in oracle_heads(w, (h,)):
+        refs = O.backward_head(geo, qh, kh, vh, doh, w.rope_theta)
+        for g, r, what in zip(got, refs, ("dq", "dk", "dv")):
+            grad_close(g, r, w, f"4k {what} head {h} (all rows)")
+
+
 @pytest.mark.parametrize("name", ["4k", "4k_corr", "ragged", "8k", "4k_d64"])
 def test_full_size_backward_sampled(U, name):
     """A layer's backward at full size (256x256, the ragged 250x380 grid,

@@ -189,6 +189,26 @@ def test_full_size_sampled_rows(U, name, fused):
     assert torch.isfinite(out.float()).all()
 
 
+@pytest.mark.parametrize("name,heads", [("4k", (0, 11, 23)), ("8k", (7,)), ("ragged", (12,)), ("4k_corr", (5,))])
+def test_full_size_whole_heads(U, name, heads):
+    """The bench's launch configuration (fused layer) at full size, every
+    row of the given heads (all text, HR and LR rows; the heads run on
+    different XCD queues) against the oracle's whole-head forward."""
+    import torch
+    w = WL.WORKLOADS[name]
+    p = plan_of(U, w)
+    q, k, v = qkv_device(w)
+    out = torch.full_like(q, float("nan"))
+    U.Layer(p, fused=True)(q, k, v, out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    geo = O.geometry_of(w)
+    for h in heads:
+        got = to_host_f64(out[0, :, h].contiguous(), w.dtype)
+        ref = O.forward_head(geo, *(WL.head_f64(w, t, h) for t in (WL.Q, WL.K, WL.V)), w.rope_theta)
+        assert_close(seg_errors(got, ref, w), tol_of(w), f"{name} head {h} (all {w.seq_len} rows)")
+
+
 @pytest.mark.parametrize("name", ["tiny", "small_ragged", "small_d64", "small_ragged_f32", "small_f32_d128", "1k",
                                   "ragged"] + CORR)
 def test_fused_entry_points_bit_exact(U, name):
