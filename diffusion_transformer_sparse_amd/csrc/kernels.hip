@@ -686,7 +686,8 @@ __device__ __forceinline__ void attn_item_f32(KArgs kp, int32_t item, char* smem
 // One bf16 query tile (plan item `item`) of the attention: the three-stage
 // pipeline described above.
 template <int D>
-__device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* smem, ug::Range* s_rng) {
+__device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* smem, ug::Range* s_rng,
+                                               int32_t* s_item) {
   using T = __bf16;
   using Lds = AttnLds<T, D>;
   constexpr int TB = Lds::kTileBytes;
@@ -959,40 +960,22 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
     step(i, std::integral_constant<int, 1>{}, sb, sa, pa, pb);
     step(i + 1, std::integral_constant<int, 0>{}, sa, sb, pb, pa);
   }
-  if (i < ntiles) {  // one odd step left; the weights of the last tile land in pb, its V in slot 1
+  if (i < ntiles)  // one odd step left; the weights of the last tile land in pb, its V in slot 1
     step(i, std::integral_constant<int, 1>{}, sb, sa, pa, pb);
-    pv_all(pb, smem + 3 * TB);
-  } else {  // the weights of the last tile (an even one) are in pa, its V in slot 0
-    pv_all(pa, smem + 2 * TB);
-  }
 
   // ---- epilogue: combine the lane halves' row sums, normalise, and write
   // the wave's 32 x D output block through LDS (swizzled rows) as full rows.
+  // The next item's cursor is taken first, so that its atomic is in flight
+  // during the epilogue, and the output rows' destinations are looked up
+  // before the last PV.
   kp = kernel_args();  // the epilogue's arguments are loaded here, not kept across the loop
-  const float total = pair_sum(lsum);
-  const float inv = 1.0f / total;
-  if (kp->lse && g == 0 && qrow < task.q1)  // log(sum_j exp(s_j)) = (mref + log2(total)) * ln 2
-    kp->lse[int64_t(blk.bh) * kp->lse_rows + qrow] = (mref + __log2f(total)) * 0.6931471805599453f;
-  __syncthreads();  // every wave has read the last V tile before the staging below overwrites it
-  char* const ost = smem + wave * 32 * RB;
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d0 = t * 32 + 8 * q4 + 4 * g;  // 4 consecutive dims
-      char* dst = ost + l32 * RB + (((d0 / Lds::kEl16) ^ Lds::k_swz(l32)) * 16) + (d0 % Lds::kEl16) * 2;
-      bf16x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = __bf16(acc[t][4 * q4 + e] * inv);
-      *reinterpret_cast<bf16x4*>(dst) = w;
-    }
-  // each wave reads back only its own block: LDS operations of one wave
-  // complete in order, so no barrier is needed between the write and read.
+  const int32_t x0 = xcc_id();
+  int32_t cnext = 0;
+  if (tid == 0) cnext = __hip_atomic_fetch_add(kp->queue + x0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   constexpr int rows_per_pass = 64 / Lds::kChunks;
   constexpr int kPasses = 32 / rows_per_pass;
-  // Destination rows first, as branch-free table reads (rows past the tile
-  // are clamped for the lookup and skipped at the store), so that all the
-  // lookups are in flight together.
+  // Destination rows as branch-free table reads (rows past the tile are
+  // clamped for the lookup and skipped at the store), all in flight together.
   int32_t orow[kPasses];
   if (kp->out_perm) {  // uniform
 #pragma unroll
@@ -1010,6 +993,41 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
     for (int pass = 0; pass < kPasses; ++pass)
       orow[pass] = task.q0 + wave * 32 + pass * rows_per_pass + lane / Lds::kChunks;
   }
+  if ((ntiles - 1) & 1)  // the weights of the last tile are in pb (odd) or pa (even), its V in that slot
+    pv_all(pb, smem + 3 * TB);
+  else
+    pv_all(pa, smem + 2 * TB);
+  const float total = pair_sum(lsum);
+  const float inv = 1.0f / total;
+  if (kp->lse && g == 0 && qrow < task.q1)  // log(sum_j exp(s_j)) = (mref + log2(total)) * ln 2
+    kp->lse[int64_t(blk.bh) * kp->lse_rows + qrow] = (mref + __log2f(total)) * 0.6931471805599453f;
+  __syncthreads();  // every wave has read the last V tile before the staging below overwrites it
+  char* const ost = smem + wave * 32 * RB;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = t * 32 + 8 * q4 + 4 * g;  // 4 consecutive dims
+      char* dst = ost + l32 * RB + (((d0 / Lds::kEl16) ^ Lds::k_swz(l32)) * 16) + (d0 % Lds::kEl16) * 2;
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = __bf16(acc[t][4 * q4 + e] * inv);
+      *reinterpret_cast<bf16x4*>(dst) = w;
+    }
+  // The next item, before the output stores (whose completion a wait on
+  // the cursor's atomic would otherwise include): the cursor taken above if
+  // it names one, else the usual search over the queues (which moves the
+  // own queue's cursor once more, as a failed grab does).
+  if (tid == 0) {
+    int32_t next;
+    if (cnext < kp->queue_len && kp->blocks[cnext * ug::kXcds + x0].task >= 0)
+      next = cnext * ug::kXcds + x0;
+    else
+      next = queue_grab(kp->queue, kp->queue_len, kp->blocks, x0);
+    *s_item = next;
+  }
+  // each wave reads back only its own block: LDS operations of one wave
+  // complete in order, so no barrier is needed between the write and read.
 #pragma unroll
   for (int pass = 0; pass < kPasses; ++pass) {
     const int r = pass * rows_per_pass + lane / Lds::kChunks;
@@ -1028,19 +1046,30 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[Lds::kTotalBytes];
   __shared__ ug::Range s_rng[ug::kAttnMaxRanges];
   __shared__ int32_t s_item;
+  if (threadIdx.x == 0) {
+    KArgs kp = kernel_args();
+    s_item = queue_grab(kp->queue, kp->queue_len, kp->blocks, xcc_id());
+  }
+  __syncthreads();
   for (;;) {
-    if (threadIdx.x == 0) {
-      KArgs kp = kernel_args();
-      s_item = queue_grab(kp->queue, kp->queue_len, kp->blocks, xcc_id());
-    }
-    __syncthreads();
     const int32_t item = s_item;
     if (item < 0) break;
-    if constexpr (std::is_same<T, __bf16>::value)
-      attn_item_bf16<D>(kernel_args(), item, smem, s_rng);
-    else
+    if constexpr (std::is_same<T, __bf16>::value) {
+      // the item names the next one in s_item before it returns
+      attn_item_bf16<D>(kernel_args(), item, smem, s_rng, &s_item);
+      // The next item reuses the LDS and reads s_item; the output stores
+      // need not have landed (an LDS-only wait, no memory fence).
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+    } else {
       attn_item_f32<D>(kernel_args(), item, smem, s_rng);
-    __syncthreads();  // the next item reuses the LDS and s_item
+      __syncthreads();  // the next item reuses the LDS and s_item
+      if (threadIdx.x == 0) {
+        KArgs kp = kernel_args();
+        s_item = queue_grab(kp->queue, kp->queue_len, kp->blocks, xcc_id());
+      }
+      __syncthreads();
+    }
   }
   if (threadIdx.x == 0) queue_finish(kernel_args()->queue);
 }
