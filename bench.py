@@ -226,32 +226,59 @@ def main():
     ums_step, uavg = timed(step_unfused, 5, max(5, args.steps // 2), 2)
     ums_perm3, ums_rope, ums_attn, ums_unperm = uavg(0, 1), uavg(1, 2), uavg(2, 3), uavg(3, 4)
 
-    backward = None
-    if w.dtype == "bf16" and not args.no_backward:
-        d_o = to_dev(WL.tensor_storage(w, WL.DO))
-        train = U.TrainLayer(plan, dev)
-        grads = [torch.empty_like(q) for _ in range(3)]
-        train.forward(q, k, v, out)
+    def measure_training(tw, steps):
+        """Training layer of workload tw: the forward that keeps the LSE
+        (permute+RoPE, permute V, attention with LSE, unpermute O) and the
+        backward step (permute dO, attention backward, RoPE transpose and
+        unpermute of dQ and dK, unpermute dV), each timed with HIP events."""
+        tplan = plan if tw is w else U.ug_plan(U.desc_of(tw))
+        tinfo = tplan.info
+        tq, tk, tv = (to_dev(WL.tensor_storage(tw, t)) for t in (WL.Q, WL.K, WL.V))
+        d_o = to_dev(WL.tensor_storage(tw, WL.DO))
+        tout = torch.empty_like(tq)
+        train = U.TrainLayer(tplan, dev)
+        grads = [torch.empty_like(tq) for _ in range(3)]
+
+        def step_fwd(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            U.ug_permute_rope(tplan, tq, tk, train.qp, train.kp)
+            U.ug_permute(tplan, tv, train.vp)
+            if ev is not None:
+                ev[1].record(stream)
+            U.ug_attn_fwd_lse(tplan, train.qp, train.kp, train.vp, train.op, train.lse)
+            if ev is not None:
+                ev[2].record(stream)
+            U.ug_unpermute(tplan, train.op, tout)
+            if ev is not None:
+                ev[3].record(stream)
 
         def step_bwd(ev=None):
             if ev is not None:
                 ev[0].record(stream)
-            U.ug_permute(plan, d_o, train.dop)
+            U.ug_permute(tplan, d_o, train.dop)
             if ev is not None:
                 ev[1].record(stream)
-            U.ug_attn_bwd(plan, train.qp, train.kp, train.vp, train.op, train.dop, train.lse, train.dq, train.dk,
+            U.ug_attn_bwd(tplan, train.qp, train.kp, train.vp, train.op, train.dop, train.lse, train.dq, train.dk,
                           train.dv, train.ws)
             if ev is not None:
                 ev[2].record(stream)
-            U.ug_permute_rope_bwd(plan, train.dq, train.dk, grads[0], grads[1])
-            U.ug_unpermute(plan, train.dv, grads[2])
+            U.ug_permute_rope_bwd(tplan, train.dq, train.dk, grads[0], grads[1])
+            U.ug_unpermute(tplan, train.dv, grads[2])
             if ev is not None:
                 ev[3].record(stream)
 
-        bms_step, bavg = timed(step_bwd, 4, max(5, args.steps // 5), 2)
-        bms_attn = bavg(1, 2)
-        bflops = 2.5 * info["eff_flops"]
-        backward = {
+        fms_step, favg = timed(step_fwd, 4, steps, 2)
+        bms_step, bavg = timed(step_bwd, 4, steps, 2)
+        fflops = tinfo["eff_flops"]
+        bflops = 2.5 * tinfo["eff_flops"]
+        fms_attn, bms_attn = favg(1, 2), bavg(1, 2)
+        res = {
+            "workload": tw.name,
+            "batch": tw.batch,
+            "forward": {"ms_per_step": round(fms_step, 4), "attn_fwd_lse_ms": round(fms_attn, 4),
+                        "eff_tflops": round(fflops / (fms_attn * 1e-3) / 1e12, 2),
+                        "frac_peak": round(fflops / (fms_attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
             "ms_per_step": round(bms_step, 4),
             "step": "ug_permute(dO) + ug_attn_bwd + ug_permute_rope_bwd(dQ,dK) + ug_unpermute(dV)",
             "attn_bwd": {"ms": round(bms_attn, 4), "eff_tflops": round(bflops / (bms_attn * 1e-3) / 1e12, 2),
@@ -259,7 +286,16 @@ def main():
                          "eff_flop": bflops},
             "layout_ms": round(bavg(0, 1) + bavg(2, 3), 4),
         }
-        del train, grads, d_o
+        del train, grads, d_o, tq, tk, tv, tout
+        return res
+
+    backward = None
+    backward_train = None
+    if w.dtype == "bf16" and not args.no_backward:
+        backward = measure_training(w, max(5, args.steps // 5))
+        # the pages' fine-tuning shape: 1024x1024 images (64x64 latent tokens)
+        # with 256x256 guides, one image per GPU
+        backward_train = measure_training(WL.WORKLOADS["1k"], max(20, args.steps))
 
     warm = None
     if not args.no_warm:
@@ -270,18 +306,27 @@ def main():
             noise = to_dev(WL.warm_storage(ww, WL.WARM_NOISE), ww.dtype)
             x_hr = torch.empty_like(noise)
 
-            def step_warm(ev=None):
+            # ten launches between two events (each a whole warm start of the
+            # batch), so that the event and launch gaps of one launch do not
+            # dominate a kernel of tens of microseconds; one launch per event
+            # pair is reported beside it
+            def step_warm(ev=None, reps=10):
                 if ev is not None:
                     ev[0].record(stream)
-                U.ug_warm_start(x_lr, noise, ww.rho, ww.alpha, ww.sharpen, x_hr)
+                for _ in range(reps):
+                    U.ug_warm_start(x_lr, noise, ww.rho, ww.alpha, ww.sharpen, x_hr)
                 if ev is not None:
                     ev[1].record(stream)
 
             _, wavg = timed(step_warm, 2, 20, 3)
-            wms = wavg(0, 1)
+            wms = wavg(0, 1) / 10
+            _, wavg1 = timed(lambda ev=None: step_warm(ev, 1), 2, 20, 3)
+            wms1 = wavg1(0, 1)
             nbytes = 2 * noise.numel() * noise.element_size() + x_lr.numel() * x_lr.element_size()
             warm[wname] = {"ms": round(wms, 4), "bytes": nbytes, "gbs": round(nbytes / (wms * 1e-3) / 1e9, 1),
-                           "frac_hbm": round(nbytes / (wms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                           "frac_hbm": round(nbytes / (wms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                           "ms_one_launch": round(wms1, 4),
+                           "frac_hbm_one_launch": round(nbytes / (wms1 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
             del x_lr, noise, x_hr
 
     esize = 2 if w.dtype == "bf16" else 4
@@ -334,6 +379,7 @@ def main():
             "unpermute_o": hbm(2 * tbytes, ums_unperm),
         },
         "backward": backward,
+        "backward_train_1k": backward_train,
         "warm_start": warm,
         "plan_build_s": round(t_plan, 4),
         "kernel_sha": kernel_hash(),

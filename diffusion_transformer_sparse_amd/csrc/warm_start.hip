@@ -17,7 +17,8 @@
 // blurred one (wb) over three consecutive LR rows (columns), and
 //   Y = sum_ij ((1 + s) wc_y[i] wc_x[j] - s wb_y[i] wb_x[j]) X_lr[y0+i][x0+j].
 // HBM-bound: every noise and output byte moves once; the LR samples a tile
-// needs are read once into LDS, where the 3x3 stencils gather them.
+// needs are read once into LDS, and each thread forms the stencil
+// separably (see the kernel).
 #include "common.hpp"
 
 #include <cmath>
@@ -77,14 +78,23 @@ __device__ __forceinline__ void load_f32(const T* p, float (&x)[16 / sizeof(T)])
 }
 
 // One workgroup per HR tile of kTileH x kTileW pixels and a block of up to
-// kVecBlock 16-byte channel vectors: the LR samples the tile's stencils touch
-// are staged once in LDS, and the per-row and per-column weights are
-// computed once; each thread then produces (pixel, vector) items with the
-// vector index fastest, so noise and output accesses are contiguous.
-constexpr int kTileH = 8, kTileW = 32, kVecBlock = 8;
-constexpr int kItems = kTileH * kTileW * kVecBlock / kWarmThreads;  // (pixel, vector) items per thread
+// kVecBlock 16-byte channel vectors; thread (column, vector) produces the
+// tile's kTileH pixels of its column, so that noise and output rows are
+// contiguous across the workgroup.  The stencil is separable: with
+//   Hc[m] = sum_j wc_x[j] X[m][x0+j],  Hb[m] = sum_j wb_x[j] X[m][x0+j]
+// (the column passes of LR row m), the pixel's value is
+//   sum_i (1 + s) wc_y[i] Hc[y0+i] - s wb_y[i] Hb[y0+i].
+// A thread keeps the column passes of three consecutive LR rows in
+// registers and slides them down as the tile's rows move to the next LR
+// row, so each LR sample is converted and weighted once per thread.
+constexpr int kTileH = 8, kVecBlock = 8, kTileW = kWarmThreads / kVecBlock;
 
 __host__ __device__ constexpr int lr_span(int tile, int rho) { return (tile + 1) / rho + 3; }
+
+struct RowWeights {  // one HR row: LR rows base .. base+2 with (1 + s) wc and s wb
+  int base;
+  float ca[3], cb[3];
+};
 
 template <typename T>
 __global__ __launch_bounds__(kWarmThreads) void warm_start_kernel(const T* __restrict__ x_lr, const T* noise,
@@ -93,7 +103,8 @@ __global__ __launch_bounds__(kWarmThreads) void warm_start_kernel(const T* __res
                                                                  int32_t C, int32_t rho, float alpha, float s) {
   constexpr int E = 16 / sizeof(T);
   extern __shared__ __attribute__((aligned(16))) char warm_smem[];
-  __shared__ AxisWeights s_ay[kTileH], s_ax[kTileW];
+  __shared__ RowWeights s_ay[kTileH];
+  __shared__ AxisWeights s_ax[kTileW];
 
   const int32_t vpp = C / E;                             // vectors per pixel
   const int32_t nvb = (vpp + kVecBlock - 1) / kVecBlock;  // vector blocks
@@ -105,6 +116,22 @@ __global__ __launch_bounds__(kWarmThreads) void warm_start_kernel(const T* __res
   const int32_t v0 = vb * kVecBlock, nv = min(kVecBlock, vpp - v0);
   const int64_t b = blockIdx.y;
   const int tid = threadIdx.x;
+  const int v = tid % kVecBlock, cl = tid / kVecBlock;
+  const int32_t c = c0 + cl;
+  const bool col_ok = v < nv && c < W;
+
+  // The thread's noise vectors first, so their loads are in flight while the
+  // LR patch is staged (rows past a ragged edge load vector 0, store nothing).
+  const u32x4* nzv = reinterpret_cast<const u32x4*>(noise) + b * int64_t(H) * W * vpp;
+  u32x4* outv = reinterpret_cast<u32x4*>(x_hr) + b * int64_t(H) * W * vpp;
+  const int64_t g0 = (int64_t(r0) * W + c) * vpp + v0 + v;
+  const int64_t row_step = int64_t(W) * vpp;
+  u32x4 nz[kTileH];
+#pragma unroll
+  for (int k = 0; k < kTileH; ++k) {
+    const bool ok = col_ok && r0 + k < H;
+    nz[k] = __builtin_nontemporal_load(nzv + (ok ? g0 + k * row_step : 0));
+  }
 
   // LR rows [y_lo, y_hi] and columns [x_lo, x_hi] the tile's stencils touch
   const int32_t y_lo = min(max(r0 - 1, 0) / rho, h - 1);
@@ -116,57 +143,87 @@ __global__ __launch_bounds__(kWarmThreads) void warm_start_kernel(const T* __res
   u32x4* const lds = reinterpret_cast<u32x4*>(warm_smem);  // [ny][nx][nv]
   const u32x4* lr = reinterpret_cast<const u32x4*>(x_lr) + b * int64_t(h) * w * vpp;
   for (int32_t i = tid; i < ny * nx * nv; i += kWarmThreads) {
-    const int32_t v = i % nv, px = i / nv;
+    const int32_t vv = i % nv, px = i / nv;
     const int32_t yy = y_lo + px / nx, xx = x_lo + px % nx;
-    lds[i] = lr[(int64_t(yy) * w + xx) * vpp + v0 + v];
+    lds[i] = lr[(int64_t(yy) * w + xx) * vpp + v0 + vv];
   }
-  if (tid < kTileH) s_ay[tid] = axis_weights(min(r0 + tid, H - 1), H, h, rho);
+  if (tid < kTileH) {
+    const AxisWeights a = axis_weights(min(r0 + tid, H - 1), H, h, rho);
+    RowWeights rw;
+    rw.base = a.base;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) rw.ca[i] = (1.f + s) * a.wc[i], rw.cb[i] = s * a.wb[i];
+    s_ay[tid] = rw;
+  }
   if (tid >= 64 && tid < 64 + kTileW) s_ax[tid - 64] = axis_weights(min(c0 + tid - 64, W - 1), W, w, rho);
   __syncthreads();
 
-  const u32x4* nzv = reinterpret_cast<const u32x4*>(noise) + b * int64_t(H) * W * vpp;
-  u32x4* outv = reinterpret_cast<u32x4*>(x_hr) + b * int64_t(H) * W * vpp;
-  for (int k = 0; k < kItems; ++k) {
-    const int32_t i = tid + k * kWarmThreads;
-    const int32_t v = i % kVecBlock, px = i / kVecBlock;
-    const int32_t r = r0 + px / kTileW, c = c0 + px % kTileW;
-    if (v >= nv || r >= H || c >= W) continue;
-    const int64_t g = (int64_t(r) * W + c) * vpp + v0 + v;
-    const u32x4 nz = __builtin_nontemporal_load(nzv + g);
-    const AxisWeights& ay = s_ay[px / kTileW];
-    const AxisWeights& ax = s_ax[px % kTileW];
-    float acc[E];
+  const AxisWeights ax = s_ax[cl];
+  int32_t lxo[3];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  // Every tap with a nonzero weight lies in the staged patch; a third tap
+  // that does not (zero weight) is clamped into it, so it reads a staged
+  // (finite) sample rather than whatever the LDS held before.
+  for (int j = 0; j < 3; ++j) lxo[j] = (min(ax.base + j, x_hi) - x_lo) * nv + v;
+  // column passes of LR row y (clamped into the patch) into hc, hb
+  auto column_pass = [&](int32_t y, float (&hc)[E], float (&hb)[E]) {
+    const int32_t lrow = (min(y, y_hi) - y_lo) * nx * nv;
 #pragma unroll
-    for (int yi = 0; yi < 3; ++yi) {
-      const int32_t ly = min(ay.base + yi, h - 1) - y_lo;
+    for (int e = 0; e < E; ++e) hc[e] = hb[e] = 0.f;
 #pragma unroll
-      for (int xj = 0; xj < 3; ++xj) {
-        const float wgt = (1.f + s) * ay.wc[yi] * ax.wc[xj] - s * ay.wb[yi] * ax.wb[xj];
-        if (wgt == 0.f) continue;
-        const int32_t lx = min(ax.base + xj, w - 1) - x_lo;
-        const u32x4 xv = lds[(ly * nx + lx) * nv + v];
-        float x[E];
-        load_f32<T>(reinterpret_cast<const T*>(&xv), x);
+    for (int j = 0; j < 3; ++j) {
+      const u32x4 xv = lds[lrow + lxo[j]];
+      float x[E];
+      load_f32<T>(reinterpret_cast<const T*>(&xv), x);
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = fmaf(wgt, x[e], acc[e]);
+      for (int e = 0; e < E; ++e) {
+        hc[e] = fmaf(ax.wc[j], x[e], hc[e]);
+        hb[e] = fmaf(ax.wb[j], x[e], hb[e]);
       }
     }
+  };
+  float hc[3][E], hb[3][E];
+  int32_t held = s_ay[0].base;  // LR row of hc[0] / hb[0] (uniform)
+#pragma unroll
+  for (int i = 0; i < 3; ++i) column_pass(held + i, hc[i], hb[i]);
+
+#pragma unroll
+  for (int k = 0; k < kTileH; ++k) {
+    const RowWeights ay = s_ay[k];
+    while (held < ay.base) {  // uniform; at most one step per row for rho >= 1
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        hc[0][e] = hc[1][e], hb[0][e] = hb[1][e];
+        hc[1][e] = hc[2][e], hb[1][e] = hb[2][e];
+      }
+      ++held;
+      column_pass(held + 2, hc[2], hb[2]);
+    }
     float nf[E];
-    load_f32<T>(reinterpret_cast<const T*>(&nz), nf);
+    load_f32<T>(reinterpret_cast<const T*>(&nz[k]), nf);
+    float o32[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float acc = ay.ca[0] * hc[0][e];
+      acc = fmaf(ay.ca[1], hc[1][e], acc);
+      acc = fmaf(ay.ca[2], hc[2][e], acc);
+      acc = fmaf(-ay.cb[0], hb[0][e], acc);
+      acc = fmaf(-ay.cb[1], hb[1][e], acc);
+      acc = fmaf(-ay.cb[2], hb[2][e], acc);
+      o32[e] = alpha * nf[e] + (1.f - alpha) * acc;
+    }
     u32x4 out;
     if constexpr (std::is_same<T, float>::value) {
       float* o = reinterpret_cast<float*>(&out);
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = alpha * nf[e] + (1.f - alpha) * acc[e];
+      for (int e = 0; e < E; ++e) o[e] = o32[e];
     } else {
       bf16x8 o;
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = __bf16(alpha * nf[e] + (1.f - alpha) * acc[e]);
+      for (int e = 0; e < E; ++e) o[e] = __bf16(o32[e]);
       out = *reinterpret_cast<u32x4*>(&o);
     }
-    __builtin_nontemporal_store(out, outv + g);
+    if (col_ok && r0 + k < H) __builtin_nontemporal_store(out, outv + g0 + k * row_step);
   }
 }
 

@@ -55,6 +55,10 @@ CASES = {
     "no_sharpen": dict(sharpen=0.0),
     "strong_sharpen": dict(sharpen=2.0),
     "one_pixel_lr": dict(lr_h=1, lr_w=1),
+    "rho8": dict(rho=8, lr_h=5, lr_w=5),           # tiles whose third LR tap lies past the staged patch
+    "rho16_ragged": dict(rho=16, lr_h=3, lr_w=3),
+    "bf16_c72": dict(dtype="bf16", channels=72),  # a partial block of channel vectors
+    "f32_c36": dict(channels=36),
     "bf16_c16": dict(dtype="bf16", channels=16),
     "batch3": dict(batch=3),
 }
