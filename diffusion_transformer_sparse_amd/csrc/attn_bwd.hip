@@ -320,16 +320,34 @@ __device__ __forceinline__ void run_queue(Item item_fn) {
 
 // ---------------------------------------------------------------------------
 // dQ: per query tile (the forward's tasks, taken from the queues), 8 waves x 32
-// queries.  Per wave and 64-key tile (K, V in two-slot LDS rings):
-//   S^T  = K Q^T     (A: K rows from LDS, B: the wave's Q in registers)
-//   dP^T = V dO^T    (A: V rows from LDS, B: the wave's dO in registers)
-//   dS^T = exp2(S^T * scale_log2 - lse2) * (dP^T - Delta)   lane = query
-//   dQ^T += K^T dS^T (A: K transposed from LDS, B: dS^T from registers)
+// queries.  Per wave, 32-key block u (half of a 64-key tile; K and V tiles
+// in three-slot LDS rings):
+//   A(u): S^T  = K Q^T     (A: K rows from LDS, B: the wave's Q in registers)
+//         dP^T = V dO^T    (A: V rows from LDS, B: the wave's dO in registers)
+//   B(u): dS^T = exp2(S^T * scale_log2 - lse2) * (dP^T - Delta)   lane = query
+//   C(u): dQ^T += K^T dS^T (A: K transposed from LDS, B: dS^T from registers)
+// Software pipeline over blocks: step u runs A(u+1) as one MFMA per slot with
+// one (or two) dS elements of B(u) beside each, then C(u).  The slots are
+// fenced so the compiler keeps the interleave; operand reads run kLead slots
+// ahead.  Ring protocol (one barrier per tile, after its first block): the
+// loads of tile i+2 are issued right after that barrier of tile i, into the
+// slots of tile i-1, whose last reads (C of its second block, and A of its
+// second block for V) come before it, and they must land by the barrier of
+// tile i+1, which the block that first reads them (A of tile i+2's first
+// block) follows.
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ void dq_item(BArgs kp, int32_t item, char* smem, ug::Range* s_rng) {
   using L = Tile<D>;
   constexpr int TB = L::kBytes;
+  constexpr int RB = L::RB;
+  constexpr int kQRegs = D / 16;           // k-steps of one 32-key block's S^T (and dP^T)
+  constexpr int kASlots = 2 * kQRegs;      // A: S^T and dP^T MFMAs, alternating
+  constexpr int kCSlots = 2 * (D / 32);    // C: two 16-key chunks x D/32 dim tiles
+  constexpr int kSlots = kASlots + kCSlots;
+  constexpr int kElPerSlot = 16 / kASlots;  // dS elements of B(u) per A slot
+  constexpr int kLead = 4;
+  static_assert(kElPerSlot * kASlots == 16, "16 dS elements per lane and block");
 
   const ug::Block blk = kp->blocks[item];
   const ug::Task task = kp->tasks[blk.task];
@@ -346,9 +364,9 @@ __device__ __forceinline__ void dq_item(BArgs kp, int32_t item, char* smem, ug::
   const int32_t nr = task.r1 - task.r0;
   if (tid < nr) s_rng[tid] = kp->ranges[task.r0 + tid];
 
-  bf16x8 qf[D / 16], df[D / 16];
+  bf16x8 qf[kQRegs], df[kQRegs];
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) {
+  for (int i = 0; i < kQRegs; ++i) {
     qf[i] = *reinterpret_cast<const bf16x8*>(kp->q + hoff + qload * rs + 16 * i + 8 * g);
     df[i] = *reinterpret_cast<const bf16x8*>(kp->d_o + hoff + qload * rs + 16 * i + 8 * g);
   }
@@ -360,6 +378,7 @@ __device__ __forceinline__ void dq_item(BArgs kp, int32_t item, char* smem, ug::
 
   int32_t ntiles = 0;
   for (int32_t r = 0; r < nr; ++r) ntiles += (s_rng[r].k1 - s_rng[r].k0 + kRows - 1) / kRows;
+  ntiles = __builtin_amdgcn_readfirstlane(ntiles);
 
   const __bf16* kg = kp->k + hoff;
   const __bf16* vg = kp->v + hoff;
@@ -367,53 +386,124 @@ __device__ __forceinline__ void dq_item(BArgs kp, int32_t item, char* smem, ug::
   ld.init(rs, tid);
   LaneOffsets<D> lo;
   lo.init(lane);
+  // Opaque offsets: with their known bits the compiler would fold the
+  // constant part of every (offset, chunk) pair into its own register and
+  // hold them all across the loop; opaque, the constant parts stay in the
+  // LDS instructions' immediate offsets.
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) asm volatile("" : "+v"(lo.row[i]));
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) asm volatile("" : "+v"(lo.tr[t][0]), "+v"(lo.tr[t][1]));
   TileCursor cur;
   cur.init(s_rng, 0, nr);
+  // K ring: slots 0..2 at [0, 3TB); V ring: slots 0..2 at [3TB, 6TB).  Tile
+  // i uses slot i % 3, known at compile time in the unrolled loop below.
+  auto issue_tile = [&](int slot) {  // the cursor's next tile into `slot`
+    const int32_t nv = cur.nv();
+    ld.issue(kg, rs, cur.ks, nv, smem + slot * TB, tid, wave);
+    ld.issue(vg, rs, cur.ks, nv, smem + (3 + slot) * TB, tid, wave);
+    cur.advance(s_rng);
+  };
 
   f32x16 acc[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
 
-  int32_t nv = cur.nv();
-  ld.issue(kg, rs, cur.ks, nv, smem, tid, wave);
-  ld.issue(vg, rs, cur.ks, nv, smem + 2 * TB, tid, wave);
-  cur.advance(s_rng);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  float e_hold = 0.f;
+  // dS element j (0..15) of a block: register j of S^T and dP^T; elements
+  // 2m and 2m+1 form one packed pair of chunk j / 8.  The volatile asm pins
+  // the work to its slot.
+  auto ds_elem = [&](const f32x16& s, const f32x16& dp, bf16x8 (&ds)[2], int j) {
+    // P <= 1 for every allowed key; the clamp (free on v_exp) keeps the zero
+    // rows of a ragged tile finite whatever the row's LSE.
+    const float pv = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(fmaf(s[j], c2, -lse2)), 0.f, 1.f);
+    const float d = pv * (dp[j] - dlt);
+    if ((j & 1) == 0) {
+      e_hold = d;
+      asm volatile("" : "+v"(e_hold));
+    } else {
+      bf16x2 pr = {__bf16(e_hold), __bf16(d)};
+      asm volatile("" : "+v"(pr));
+      ds[j >> 3][(j & 7) - 1] = pr[0];
+      ds[j >> 3][j & 7] = pr[1];
+    }
+  };
+
+  // One block step: A of the next block (rows 32 mbA .. of the K and V tiles
+  // at ka, va) into s_out / dp_out beside B of the current block (s_in,
+  // dp_in -> ds), then C of the current block (the K tile at kc, chunks
+  // 2 mbC and 2 mbC + 1).
+  auto block_step = [&](const char* ka, const char* va, int mbA, const f32x16& s_in, const f32x16& dp_in,
+                        f32x16& s_out, f32x16& dp_out, const char* kc, int mbC) {
+    bf16x8 opnd[kLead + 1];
+    bf16x8 ds[2];
+    auto fetch = [&](int k) {
+      if (k < kASlots) {  // even: K rows of k-step k/2; odd: V rows
+        const char* base = ((k & 1) ? va : ka) + mbA * 32 * RB;
+        opnd[k % (kLead + 1)] = *reinterpret_cast<const bf16x8*>(base + lo.row[k >> 1]);
+      } else {  // C: chunk 2 mbC + c / (D/32), dim tile c % (D/32)
+        const int c = k - kASlots;
+        opnd[k % (kLead + 1)] = tr_operand<D>(kc, c % (D / 32), 2 * mbC + c / (D / 32), lo);
+      }
+    };
+#pragma unroll
+    for (int k = 0; k < kLead; ++k) fetch(k);
+#pragma unroll
+    for (int k = 0; k < kSlots; ++k) {
+      if (k + kLead < kSlots) fetch(k + kLead);
+      if (k < kASlots) {
+        const int ks = k >> 1;
+        if ((k & 1) == 0)
+          s_out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[k % (kLead + 1)], qf[ks], ks == 0 ? f32x16{} : s_out,
+                                                          0, 0, 0);
+        else
+          dp_out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[k % (kLead + 1)], df[ks],
+                                                           ks == 0 ? f32x16{} : dp_out, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < kElPerSlot; ++e) ds_elem(s_in, dp_in, ds, k * kElPerSlot + e);
+      } else {
+        const int c = k - kASlots;
+        acc[c % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[k % (kLead + 1)], ds[c / (D / 32)],
+                                                                    acc[c % (D / 32)], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // prologue: tiles 0 and 1 into their slots, then A of block (0, 0)
+  issue_tile(0);
+  if (ntiles > 1) issue_tile(1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  f32x16 sa, dpa, sb, dpb;
+  sa = rows_x_regs<D>(smem, 0, qf, lo);
+  dpa = rows_x_regs<D>(smem + 3 * TB, 0, df, lo);
 
-  for (int32_t i = 0; i < ntiles; ++i) {
-    const int slot = i & 1;
-    const int32_t nv_next = cur.nv();
-    if (i + 1 < ntiles) {
-      ld.issue(kg, rs, cur.ks, nv_next, smem + (slot ^ 1) * TB, tid, wave);
-      ld.issue(vg, rs, cur.ks, nv_next, smem + 2 * TB + (slot ^ 1) * TB, tid, wave);
-      cur.advance(s_rng);
-    }
-    const char* kt = smem + slot * TB;
-    const char* vt = smem + 2 * TB + slot * TB;
-    bf16x8 dsb[4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      f32x16 s = rows_x_regs<D>(kt, mb, qf, lo);
-      const f32x16 dp = rows_x_regs<D>(vt, mb, df, lo);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = 32 * mb + 8 * (j >> 2) + 4 * g + (j & 3);
-        // P <= 1 for every allowed key; the clamp (free on v_exp) keeps
-        // the zero rows of a ragged tile finite whatever the row's LSE.
-        const float pv = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(fmaf(s[j], c2, -lse2)), 0.f, 1.f);
-        dsb[2 * mb + (j >> 3)][j & 7] = __bf16(pv * (dp[j] - dlt));
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kt, t, c, lo), dsb[c], acc[t], 0, 0, 0);
-    nv = nv_next;
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of the next tile have landed
-    __syncthreads();
+  // Tile i (in slot S = i % 3): block (i, 0) is A(i, 1) || B(i, 0), C(i, 0);
+  // then the barrier, the loads of tile i+2 into slot (S + 2) % 3, and block
+  // (i, 1): A(i+1, 0) || B(i, 1), C(i, 1).  Past the last tile, A reads a
+  // stale slot and its result is unused.
+  auto tile = [&](int32_t i, auto slot) {
+    constexpr int S = decltype(slot)::value;
+    const char* kt = smem + S * TB;
+    block_step(kt, smem + (3 + S) * TB, 1, sa, dpa, sb, dpb, kt, 0);
+    __builtin_amdgcn_s_waitcnt(0);  // tile i+1 has landed (issued two blocks ago)
+    __syncthreads();                // and every wave is past tile i-1's slots
+    if (i + 2 < ntiles) issue_tile((S + 2) % 3);
+    block_step(smem + ((S + 1) % 3) * TB, smem + (3 + (S + 1) % 3) * TB, 0, sb, dpb, sa, dpa, kt, 1);
+  };
+  // groups of three tiles, so that every slot is a compile-time offset; the
+  // loop has no exit inside a group
+  int32_t i = 0;
+  for (; i + 3 <= ntiles; i += 3) {
+    tile(i, std::integral_constant<int, 0>{});
+    tile(i + 1, std::integral_constant<int, 1>{});
+    tile(i + 2, std::integral_constant<int, 2>{});
   }
+  if (i < ntiles) tile(i, std::integral_constant<int, 0>{});
+  if (i + 1 < ntiles) tile(i + 1, std::integral_constant<int, 1>{});
+  __syncthreads();  // every wave is done with the rings before the output staging
   kp = bwd_args();  // the epilogue's arguments are loaded here, not kept across the loop
   store_block<D>(acc, kp->scale, smem + wave * 32 * L::RB, kp->dq + hoff, rs, task.q0 + wave * 32, task.q1, lane);
 }
@@ -421,7 +511,7 @@ __device__ __forceinline__ void dq_item(BArgs kp, int32_t item, char* smem, ug::
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(BwdParams p) {
   (void)p;  // read through bwd_args()
-  run_queue<4 * Tile<D>::kBytes>([](BArgs kp, int32_t item, char* smem, ug::Range* s_rng) {  // K ring, V ring
+  run_queue<6 * Tile<D>::kBytes>([](BArgs kp, int32_t item, char* smem, ug::Range* s_rng) {  // K ring, V ring
     dq_item<D>(kp, item, smem, s_rng);
   });
 }
