@@ -3,7 +3,7 @@
 block-sparse attention, inverse permutation.  Python side of the C ABI in
 include/ultragen.h; all compute runs in the library's HIP kernels."""
 from ._binding import (  # noqa: F401
-    EXPORTED, LIB_PATH, UG_BF16, UG_F32, UG_PLAN_HOST_ONLY, Layer, Plan, TrainLayer, UgDesc, UgError, UgInfo,
+    EXPORTED, LIB_PATH, UG_BF16, UG_F32, UG_PLAN_HOST_ONLY, UG_PLAN_NO_LR, Layer, Plan, TrainLayer, UgDesc, UgError, UgInfo,
     UgWarmDesc, ug_warm_start,
     bwd_workspace, desc_of, lib, make_desc, ug_attn_bwd, ug_attn_bwd_noalloc, ug_attn_fwd, ug_attn_fwd_lse, ug_attn_fwd_raster,
     ug_last_error, ug_permute, ug_permute_rope, ug_plan, ug_plan_export, ug_plan_export_blocks, ug_plan_export_lr,

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libultragen
 UG_OK, UG_ERR_INVALID_ARGUMENT, UG_ERR_UNSUPPORTED, UG_ERR_OUT_OF_MEMORY, UG_ERR_HIP, UG_ERR_INTERNAL = range(6)
 UG_F32, UG_BF16 = 0, 1
 UG_PLAN_HOST_ONLY = 1
+UG_PLAN_NO_LR = 2
 
 EXPORTED = ("ug_plan", "ug_plan_free", "ug_plan_info", "ug_plan_export", "ug_plan_export_lr", "ug_plan_export_queues",
             "ug_plan_export_blocks", "ug_permute",
@@ -119,10 +120,18 @@ def _check(fn, status):
 
 def make_desc(hr_h, hr_w, lr_h, lr_w, n_text, heads, head_dim, dtype="bf16", window=16, radius=1, rho=4,
               rope_theta=10000.0, batch=1, host_only=False, lr_mode=0) -> UgDesc:
+    """lr_h = lr_w = 0: no LR tokens (flag UG_PLAN_NO_LR); None, None: the
+    grid the coordinate scaling implies, ceil(hr_h/rho) x ceil(hr_w/rho)
+    (the C-ABI's 0 x 0)."""
+    flags = UG_PLAN_HOST_ONLY if host_only else 0
+    if lr_h is None and lr_w is None:
+        lr_h = lr_w = 0
+    elif lr_h == 0 and lr_w == 0:
+        flags |= UG_PLAN_NO_LR
     return UgDesc(batch=batch, heads=heads, head_dim=head_dim, hr_h=hr_h, hr_w=hr_w, lr_h=lr_h, lr_w=lr_w,
                   n_text=n_text, window=window, radius=radius, rho=rho,
                   dtype=UG_BF16 if dtype in ("bf16", UG_BF16) else UG_F32,
-                  flags=UG_PLAN_HOST_ONLY if host_only else 0, lr_mode=lr_mode, rope_theta=rope_theta)
+                  flags=flags, lr_mode=lr_mode, rope_theta=rope_theta)
 
 
 def desc_of(w, host_only=False) -> UgDesc:

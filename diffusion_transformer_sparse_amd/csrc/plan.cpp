@@ -50,6 +50,10 @@ ug_status validate(const ug_desc* d) {
     return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: head_dim must be a positive multiple of 4");
   if (d->hr_h < 1 || d->hr_w < 1) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: hr_h and hr_w must be >= 1");
   if (d->lr_h < 0 || d->lr_w < 0) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: lr_h and lr_w must be >= 0");
+  if ((d->lr_h == 0) != (d->lr_w == 0))
+    return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: lr_h and lr_w must both be 0 (default or none) or both > 0");
+  if ((d->flags & UG_PLAN_NO_LR) && d->lr_h != 0)
+    return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: UG_PLAN_NO_LR needs lr_h = lr_w = 0");
   if (d->n_text < 0) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: n_text must be >= 0");
   if (d->window < 1) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: window must be >= 1");
   if (d->radius < 0) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: radius must be >= 0");
@@ -57,7 +61,7 @@ ug_status validate(const ug_desc* d) {
   if (!(d->rope_theta > 0.0) || !std::isfinite(d->rope_theta))
     return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: rope_theta must be finite and > 0");
   if (d->dtype != UG_F32 && d->dtype != UG_BF16) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: unknown dtype");
-  if (d->flags & ~UG_PLAN_HOST_ONLY) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: unknown flags");
+  if (d->flags & ~(UG_PLAN_HOST_ONLY | UG_PLAN_NO_LR)) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: unknown flags");
   if (d->lr_mode != 0 && d->lr_mode != 1) return fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: lr_mode must be 0 or 1");
   const int64_t N = int64_t(d->hr_h) * d->hr_w;
   const int64_t Nlr = int64_t(d->lr_h) * d->lr_w;
@@ -561,10 +565,18 @@ ug_status alloc_queue(ug_plan_s* p) {
 
 extern "C" {
 
-ug_status ug_plan(const ug_desc* desc, ug_plan_t* out) {
+ug_status ug_plan(const ug_desc* user_desc, ug_plan_t* out) {
   ug::clear_error();
   if (!out) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: out is NULL");
   *out = nullptr;
+  if (!user_desc) return ug::fail(UG_ERR_INVALID_ARGUMENT, "ug_plan: desc is NULL");
+  // 0 x 0 LR grid: the one the coordinate scaling implies, unless NO_LR
+  ug_desc resolved = *user_desc;
+  if (resolved.lr_h == 0 && resolved.lr_w == 0 && !(resolved.flags & UG_PLAN_NO_LR) && resolved.rho >= 1) {
+    resolved.lr_h = int32_t((int64_t(resolved.hr_h) + resolved.rho - 1) / resolved.rho);
+    resolved.lr_w = int32_t((int64_t(resolved.hr_w) + resolved.rho - 1) / resolved.rho);
+  }
+  const ug_desc* desc = &resolved;
   ug_status s = ug::validate(desc);
   if (s != UG_OK) return s;
   ug_plan_s* p = new (std::nothrow) ug_plan_s;

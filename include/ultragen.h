@@ -62,13 +62,18 @@ typedef enum ug_dtype { UG_F32 = 0, UG_BF16 = 1 } ug_dtype;
 #define UG_PLAN_HOST_ONLY 1 /* build host tables only: no HIP call; only
                                ug_plan_info / ug_plan_export / ug_plan_free
                                may then be used */
+#define UG_PLAN_NO_LR 2     /* no LR tokens (lr_h and lr_w must then be 0) */
 
 /*
  * Geometry of one attention layer.
  *  - hr_h x hr_w: HR latent token grid (关键设计 1: X in R^{H x W}).
- *  - lr_h x lr_w: LR guidance grid (关键设计 2: X_lr in R^{h x w}); given
- *    explicitly (0 x anything = no LR tokens).  LR token (m, n) takes RoPE
- *    position (rho*m, rho*n) (关键设计 2, the coordinate-scaling equation).
+ *  - lr_h x lr_w: LR guidance grid (关键设计 2: X_lr in R^{h x w}).  0 x 0
+ *    means the grid the scaling implies, ceil(hr_h/rho) x ceil(hr_w/rho)
+ *    (one LR token per rho x rho block of HR tokens); flag UG_PLAN_NO_LR
+ *    (with 0 x 0) means no LR tokens; exactly one of them 0 is an error.
+ *    LR token (m, n) takes RoPE position (rho*m, rho*n) (关键设计 2, the
+ *    coordinate-scaling equation).  ug_plan_info and the exports report the
+ *    grid the plan uses.
  *  - window: l, the window side in tokens (l = 16 in 关键设计 1).  Windows
  *    of more than 256 tokens are split into several query tiles.
  *  - radius: HR queries see HR keys whose window is within Chebyshev

@@ -102,7 +102,12 @@ int main() {
   exercise(desc(32, 32, 8, 8, 16, 1, 0, 2, 64), "tiny");
   exercise(desc(48, 48, 12, 12, 16, 1, 1, 2, 64), "tiny corr");
   exercise(desc(37, 45, 11, 13, 9, 1, 1, 2, 64), "overhanging corr");
-  exercise(desc(40, 56, 0, 0, 0, 1, 0, 3), "no text, no LR");
+  {
+    ug_desc none = desc(40, 56, 0, 0, 0, 1, 0, 3);
+    none.flags |= UG_PLAN_NO_LR;
+    exercise(none, "no text, no LR");
+  }
+  exercise(desc(40, 56, 0, 0, 0, 1, 0, 3), "no text, default LR grid");
   exercise(desc(64, 64, 16, 16, 512, 1, 0), "1K");
   exercise(desc(256, 256, 64, 64, 512, 1, 0), "4K");
   exercise(desc(256, 256, 64, 64, 512, 1, 1), "4K corr");
@@ -123,6 +128,19 @@ int main() {
   bad = desc(16, 16, 4, 4, 0, 1, 2);
   expect(ug_plan(&bad, &p) == UG_ERR_INVALID_ARGUMENT && p == nullptr, "lr_mode 2 rejected", "validation");
   expect(ug_plan(nullptr, &p) == UG_ERR_INVALID_ARGUMENT, "NULL descriptor rejected", "validation");
+  bad = desc(16, 16, 0, 4, 0, 1, 0);
+  expect(ug_plan(&bad, &p) == UG_ERR_INVALID_ARGUMENT && p == nullptr, "one zero LR side rejected", "validation");
+  bad = desc(16, 16, 4, 4, 0, 1, 0);
+  bad.flags |= UG_PLAN_NO_LR;
+  expect(ug_plan(&bad, &p) == UG_ERR_INVALID_ARGUMENT && p == nullptr, "NO_LR with an LR grid rejected", "validation");
+  {  // 0 x 0 without the flag: ceil(H/rho) x ceil(W/rho)
+    ug_desc dflt = desc(37, 45, 0, 0, 8, 1, 0, 2, 64);
+    ug_plan_t q = nullptr;
+    ug_info info;
+    expect(ug_plan(&dflt, &q) == UG_OK && ug_plan_info(q, &info) == UG_OK && info.n_lr == 10 * 12,
+           "default LR grid", "resolution");
+    ug_plan_free(q);
+  }
   slot_ring();
   if (failures) return 1;
   std::printf("ok\n");

@@ -132,6 +132,32 @@ def test_descriptor_validation(field, value, status):
     assert "ug_plan" in U.ug_last_error()
 
 
+@pytest.mark.parametrize("H,W,rho", [(32, 32, 4), (37, 45, 4), (250, 380, 4), (40, 36, 3), (17, 5, 1)])
+def test_zero_lr_grid_is_the_scaled_grid(H, W, rho):
+    """A 0 x 0 LR grid is the one the coordinate scaling implies (one LR
+    token per rho x rho block, ceil division); UG_PLAN_NO_LR gives none.
+    (UltraGen notes, 关键设计 2: LR positions scaled by rho.)"""
+    dflt = U.ug_plan(U.make_desc(H, W, None, None, 8, 2, 64, "f32", rho=rho, host_only=True))
+    assert dflt.info["n_lr"] == -(-H // rho) * -(-W // rho)
+    explicit = U.ug_plan(U.make_desc(H, W, -(-H // rho), -(-W // rho), 8, 2, 64, "f32", rho=rho, host_only=True))
+    a, b = U.ug_plan_export_blocks(dflt), U.ug_plan_export_blocks(explicit)
+    assert a.keys() == b.keys() and all(np.array_equal(a[k], b[k]) for k in a)
+    assert dflt.info["seq_len"] == explicit.info["seq_len"]
+    none = U.ug_plan(U.make_desc(H, W, 0, 0, 8, 2, 64, "f32", rho=rho, host_only=True))
+    assert none.info["n_lr"] == 0 and none.info["seq_len"] == 8 + H * W
+
+
+def test_lr_grid_flag_errors():
+    d = U.make_desc(16, 16, 4, 4, 0, 2, 64, "f32", host_only=True)
+    d.flags |= U.UG_PLAN_NO_LR
+    with pytest.raises(U.UgError):
+        U.ug_plan(d)
+    d = U.make_desc(16, 16, 4, 4, 0, 2, 64, "f32", host_only=True)
+    d.lr_h = 0
+    with pytest.raises(U.UgError):
+        U.ug_plan(d)
+
+
 def test_host_only_plan_rejects_device_calls():
     p = _host_plan(WORKLOADS["tiny"])
     lib = U.lib()
