@@ -243,8 +243,10 @@ ug_status ug_rope2d(ug_plan_t plan, void* q_perm, void* k_perm, void* stream);
  * same windows (lr_mode 1); an LR query sees LR and text.  Masked keys are
  * excluded (additive -inf).  O is written in the permuted layout.  bf16: bf16
  * MFMA products, fp32 softmax and accumulation, O rounded to nearest even;
- * fp32: fp32 MFMA throughout.  `workspace` may be NULL when
- * info.workspace_bytes is 0.  o must not overlap q, k or v.
+ * fp32: fp32 MFMA throughout.  `workspace` is part of the boundary's
+ * signature but not read: info.workspace_bytes is 0 for every plan (the
+ * kernels' work-queue cursors live in the plan), so it may be NULL.  o must
+ * not overlap q, k or v.
  */
 ug_status ug_attn_fwd(ug_plan_t plan, const void* q, const void* k, const void* v, void* o,
                       void* workspace, void* stream);
