@@ -14,6 +14,9 @@ from ctypes import POINTER, byref, c_char_p, c_double, c_int32, c_int64, c_void_
 import numpy as np
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libultragen.so")
+# the same sources built with index checks that record violations in a device
+# word (UG_BOUNDS_CHECK); see use_library and debug_bounds
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libultragen_debug.so")
 
 UG_OK, UG_ERR_INVALID_ARGUMENT, UG_ERR_UNSUPPORTED, UG_ERR_OUT_OF_MEMORY, UG_ERR_HIP, UG_ERR_INTERNAL = range(6)
 UG_F32, UG_BF16 = 0, 1
@@ -60,14 +63,32 @@ class UgError(RuntimeError):
 _lib = None
 
 
+_libs = {}
+
+
+def use_library(path: str = LIB_PATH):
+    """Make every entry point of this module call the library at `path`
+    (LIB_PATH, or DEBUG_LIB_PATH for the bounds-checking build).  Plans are
+    tied to the library that built them."""
+    global _lib
+    _lib = _load(path)
+    return _lib
+
+
 def lib():
     """Load libultragen.so once; raise if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+def _load(path):
+    if path not in _libs:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
                                "`python -m diffusion_transformer_sparse_amd.build` (no fallback exists)")
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         L.ug_plan.argtypes = [POINTER(UgDesc), POINTER(c_void_p)]
         L.ug_plan_free.argtypes = [c_void_p]
         L.ug_plan_info.argtypes = [c_void_p, POINTER(UgInfo)]
@@ -97,8 +118,30 @@ def lib():
                      "ug_rope2d", "ug_attn_fwd", "ug_permute_rope", "ug_attn_fwd_raster", "ug_attn_fwd_lse",
                      "ug_attn_bwd", "ug_attn_bwd_noalloc", "ug_rope2d_bwd", "ug_permute_rope_bwd", "ug_warm_start"):
             getattr(L, name).restype = c_int32
-        _lib = L
-    return _lib
+        for name in DEBUG_EXPORTED:
+            if hasattr(L, name):
+                getattr(L, name).argtypes = [c_void_p, c_int32]
+                getattr(L, name).restype = c_int32
+        _libs[path] = L
+    return _libs[path]
+
+
+DEBUG_EXPORTED = ("ug_debug_bounds_fwd", "ug_debug_bounds_bwd", "ug_debug_bounds_warm")
+
+
+def debug_bounds(clear: bool = True) -> dict:
+    """Violation words of the debug build's kernels (forward and layout,
+    backward, warm start), each cleared after reading if `clear`; raises on the
+    release build, which has no such words."""
+    L = lib()
+    out = {}
+    for name in DEBUG_EXPORTED:
+        if not hasattr(L, name):
+            raise RuntimeError("debug_bounds needs the debug build (use_library(DEBUG_LIB_PATH))")
+        w = ctypes.c_uint32(0)
+        _check(name, getattr(L, name)(ctypes.byref(w), int(clear)))
+        out[name[len("ug_debug_bounds_"):]] = w.value
+    return out
 
 
 def status_name(s: int) -> str:
@@ -145,14 +188,15 @@ class Plan:
 
     def __init__(self, desc: UgDesc):
         h = c_void_p()
-        _check("ug_plan", lib().ug_plan(byref(desc), byref(h)))
+        self.lib = lib()  # the library that built the plan frees it
+        _check("ug_plan", self.lib.ug_plan(byref(desc), byref(h)))
         self.handle = h
         self.desc = desc
         self.info = ug_plan_info(self)
 
     def close(self):
         if self.handle:
-            lib().ug_plan_free(self.handle)
+            self.lib.ug_plan_free(self.handle)
             self.handle = None
 
     def __del__(self):

@@ -7,6 +7,10 @@ layout, RoPE and attention forward; csrc/attn_bwd.hip: attention backward;
 csrc/warm_start.hip: the warm-start latent)
 with hipcc and links them into diffusion_transformer_sparse_amd/libultragen.so.
 All device code is built with packed-fp32 instructions disabled.
+
+The same sources built with -DUG_BOUNDS_CHECK give libultragen_debug.so, the
+debug build whose kernels record failed index checks in a device word
+(ug_debug_bounds_fwd / _bwd / _warm) instead of trapping.
 """
 from __future__ import annotations
 
@@ -18,6 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libultragen.so")
+DEBUG_OUT = os.path.join(HERE, "libultragen_debug.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -40,19 +45,27 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    plan_o = os.path.join(BUILD_DIR, "plan.o")
-    _run([HIPCC, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, "plan.cpp"),
+def _build_one(out: str, build_dir: str, defines, verbose: bool) -> str:
+    os.makedirs(build_dir, exist_ok=True)
+    plan_o = os.path.join(build_dir, "plan.o")
+    _run([HIPCC, *COMMON, *defines, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, "plan.cpp"),
           "-o", plan_o], verbose)
     objs = [plan_o]
     for src in DEVICE_SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        _run([HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+        _run([HIPCC, *COMMON, *defines, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
-    tmp = OUT + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, "-o", tmp], verbose)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """Build libultragen.so, and (debug=True) the bounds-checking libultragen_debug.so."""
+    _build_one(OUT, BUILD_DIR, [], verbose)
+    if debug:
+        _build_one(DEBUG_OUT, os.path.join(BUILD_DIR, "debug"), ["-DUG_BOUNDS_CHECK"], verbose)
     return OUT
 
 

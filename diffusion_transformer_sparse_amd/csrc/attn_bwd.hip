@@ -289,6 +289,7 @@ struct BwdParams {
   float scale;       // 1 / sqrt(D)
   int32_t* queue;     // this launch's cursor slot: 8 per-XCD queue cursors, then the finished-workgroup count
   int32_t queue_len;  // items per XCD queue (blocks / 8)
+  int32_t L, n_tasks, n_bh;  // rows, tasks of the current pass and batch*heads (index checks of the debug build)
 };
 typedef __attribute__((address_space(4))) const BwdParams* BArgs;
 __device__ __forceinline__ BArgs bwd_args() { return opaque_args<BwdParams>(); }
@@ -349,8 +350,11 @@ __device__ __forceinline__ void dq_item(BArgs kp, int32_t item, char* smem, ug::
   constexpr int kLead = 4;
   static_assert(kElPerSlot * kASlots == 16, "16 dS elements per lane and block");
 
+  UG_CHECK(item >= 0 && item < kp->queue_len * ug::kXcds, 0);
   const ug::Block blk = kp->blocks[item];
+  UG_CHECK(blk.task >= 0 && blk.task < kp->n_tasks && blk.bh >= 0 && blk.bh < kp->n_bh, 0);
   const ug::Task task = kp->tasks[blk.task];
+  UG_CHECK(task.q0 >= 0 && task.q0 < task.q1 && task.q1 <= kp->L && task.q1 - task.q0 <= ug::kAttnQueryTile, 1);
   const int32_t b = blk.bh / kp->heads, h = blk.bh - b * kp->heads;
   const int64_t hoff = int64_t(b) * kp->batch_stride + int64_t(h) * D;
   const int64_t rs = kp->row_stride;
@@ -362,7 +366,12 @@ __device__ __forceinline__ void dq_item(BArgs kp, int32_t item, char* smem, ug::
   const int32_t qload = min(qrow, task.q1 - 1);
 
   const int32_t nr = task.r1 - task.r0;
-  if (tid < nr) s_rng[tid] = kp->ranges[task.r0 + tid];
+  UG_CHECK(nr >= 1 && nr <= ug::kAttnMaxRanges, 1);
+  if (tid < nr) {
+    const ug::Range r = kp->ranges[task.r0 + tid];
+    UG_CHECK(r.k0 >= 0 && r.k0 < r.k1 && r.k1 <= kp->L, 1);
+    s_rng[tid] = r;
+  }
 
   bf16x8 qf[kQRegs], df[kQRegs];
 #pragma unroll
@@ -370,6 +379,7 @@ __device__ __forceinline__ void dq_item(BArgs kp, int32_t item, char* smem, ug::
     qf[i] = *reinterpret_cast<const bf16x8*>(kp->q + hoff + qload * rs + 16 * i + 8 * g);
     df[i] = *reinterpret_cast<const bf16x8*>(kp->d_o + hoff + qload * rs + 16 * i + 8 * g);
   }
+  UG_CHECK(qload < kp->Lp, 3);
   const int64_t srow = int64_t(blk.bh) * kp->Lp + qload;
   const float lse2 = kp->lse2[srow];
   const float dlt = kp->delta[srow];
@@ -539,7 +549,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
 
   const ug::Block blk = p.blocks[blockIdx.x];
   if (blk.task < 0) return;  // idle workgroup (uniform)
+  UG_CHECK(blk.task < p.n_tasks && blk.bh >= 0 && blk.bh < p.n_bh, 0);
   const ug::Task task = p.tasks[blk.task];
+  UG_CHECK(task.q0 >= 0 && task.q0 < task.q1 && task.q1 <= p.L && task.q1 - task.q0 <= ug::kAttnQueryTile, 1);
   const int32_t b = blk.bh / p.heads, h = blk.bh - b * p.heads;
   const int64_t hoff = int64_t(b) * p.batch_stride + int64_t(h) * D;
   const int64_t rs = p.row_stride;
@@ -549,7 +561,12 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int32_t kload = min(krow, task.q1 - 1);
 
   const int32_t nr = task.r1 - task.r0;
-  if (tid < nr) s_rng[tid] = p.ranges[task.r0 + tid];
+  UG_CHECK(nr >= 1 && nr <= ug::kAttnMaxRanges, 1);
+  if (tid < nr) {
+    const ug::Range r = p.ranges[task.r0 + tid];
+    UG_CHECK(r.k0 >= 0 && r.k0 < r.k1 && r.k1 <= p.L, 1);
+    s_rng[tid] = r;
+  }
   // Which of the tile's query ranges this lane's key sees (all of them
   // unless the tile groups corresponding-LR windows).
   const int32_t moff = p.mask_off ? p.mask_off[blk.task] : -1;  // uniform
@@ -680,6 +697,9 @@ ug_status launch_bwd(ug_plan_t p, BwdParams bp, const __bf16* o, const float* ls
   bp.tasks = p->d_tasks;
   bp.ranges = p->d_ranges;
   bp.blocks = p->d_blocks;
+  bp.L = int32_t(p->L);
+  bp.n_tasks = int32_t(p->tasks.size());
+  bp.n_bh = p->d.batch * p->d.heads;
   if (!p->blocks.empty()) {
     bp.queue_len = int32_t(p->blocks.size() / ug::kXcds);
     const unsigned grid = unsigned(std::min<size_t>(size_t(p->cus), p->blocks.size()));
@@ -693,6 +713,7 @@ ug_status launch_bwd(ug_plan_t p, BwdParams bp, const __bf16* o, const float* ls
   bp.tasks = p->d_ktasks;
   bp.ranges = p->d_kranges;
   bp.blocks = p->d_kblocks;
+  bp.n_tasks = int32_t(p->ktasks.size());
   bp.mask_off = p->d_kmask_off;
   bp.masks = p->d_kmasks;
   if (!p->kblocks.empty())
@@ -824,3 +845,5 @@ ug_status ug_attn_bwd_noalloc(ug_plan_t p, const void* q, const void* k, const v
 }
 
 }  // extern "C"
+
+UG_BOUNDS_ACCESSOR(ug_debug_bounds_bwd)

@@ -10,6 +10,42 @@
 
 #include "plan_internal.hpp"
 
+// Debug build (compiled with -DUG_BOUNDS_CHECK into libultragen_debug.so):
+// UG_CHECK(cond, bit) records a failed index check as bit `bit` of the
+// translation unit's violation word instead of trapping, so a test can read
+// the word back after its launches (ug_debug_bounds_*).  Bits:
+//   0 work item, task or (batch, head) index outside its table
+//   1 key or query range outside [0, L), inverted, or more ranges than staged
+//   2 tile load window past the sequence
+//   3 destination row of an output or statistics store outside its array
+//   4 permutation-table value outside its range
+//   5 warm start: LR patch index outside the staged patch, or a tensor index
+//     outside the tensor
+// In the release build the condition is not evaluated.
+#ifdef UG_BOUNDS_CHECK
+namespace {
+__device__ uint32_t ug_bounds_word;
+}
+#define UG_CHECK(cond, bit)                                                                                     \
+  do {                                                                                                          \
+    if (!(cond)) __hip_atomic_fetch_or(&ug_bounds_word, 1u << (bit), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); \
+  } while (0)
+// extern "C" accessor of the word: copies it to *out, then clears it if asked
+#define UG_BOUNDS_ACCESSOR(name)                                                                         \
+  extern "C" ug_status name(uint32_t* out, int32_t clear) {                                              \
+    if (!out) return ug::fail(UG_ERR_INVALID_ARGUMENT, #name ": out is NULL");                            \
+    if (hipMemcpyFromSymbol(out, HIP_SYMBOL(ug_bounds_word), sizeof(uint32_t)) != hipSuccess)             \
+      return ug::fail(UG_ERR_HIP, #name ": hipMemcpyFromSymbol failed");                                  \
+    const uint32_t zero = 0;                                                                             \
+    if (clear && hipMemcpyToSymbol(HIP_SYMBOL(ug_bounds_word), &zero, sizeof(uint32_t)) != hipSuccess)   \
+      return ug::fail(UG_ERR_HIP, #name ": hipMemcpyToSymbol failed");                                    \
+    return UG_OK;                                                                                        \
+  }
+#else
+#define UG_CHECK(cond, bit) ((void)0)
+#define UG_BOUNDS_ACCESSOR(name)
+#endif
+
 namespace ug {
 namespace dev {
 

@@ -58,6 +58,7 @@ __global__ __launch_bounds__(1024) void row_gather_kernel(const u32x4* __restric
       const int32_t j = row0 + r;
       if (j < L) {
         const int32_t s = (j < T) ? j : (j < T + N) ? T + table[j - T] : lr_table ? T + N + lr_table[j - T - N] : j;
+        UG_CHECK(s >= 0 && s < L && (j < T) == (s < T) && (j >= T + N) == (s >= T + N), 4);
         v[r] = __builtin_nontemporal_load(src + int64_t(s) * units + c);
       }
     }
@@ -212,6 +213,7 @@ __global__ __launch_bounds__(1024) void permute_rope_kernel(const T* __restrict_
     pc[r] = 0;
     if (j >= T0 && j < T0 + N) {
       const int32_t t = tab_hr[j - T0];
+      UG_CHECK(t >= 0 && t < N, 4);
       const int32_t idx = kBwd ? j - T0 : t;  // raster HR index of the rotated row
       src[r] = T0 + t;
       pr[r] = idx / W;
@@ -219,6 +221,7 @@ __global__ __launch_bounds__(1024) void permute_rope_kernel(const T* __restrict_
     } else if (j >= T0 + N) {
       const int32_t li = j - T0 - N;
       const int32_t t = tab_lr ? tab_lr[li] : li;
+      UG_CHECK(t >= 0 && t < L - T0 - N, 4);
       const int32_t i = kBwd ? li : t;  // raster LR index of the rotated row
       src[r] = T0 + N + t;
       const int32_t m = i / lr_w;
@@ -360,6 +363,7 @@ struct AttnParams {
   int64_t lse_rows;
   int32_t* queue;     // this launch's cursor slot: 8 per-XCD queue cursors, then the finished-workgroup count
   int32_t queue_len;  // items per XCD queue (blocks / 8)
+  int32_t L, n_tasks, n_bh;  // rows, tasks and batch*heads (index checks of the debug build)
 };
 
 
@@ -460,8 +464,11 @@ __device__ __forceinline__ void attn_item_f32(KArgs kp, int32_t item, char* smem
   constexpr int TB = Lds::kTileBytes;
   // K ring at [0, 2*TB), V ring at [2*TB, 4*TB)
 
+  UG_CHECK(item >= 0 && item < kp->queue_len * ug::kXcds, 0);
   const ug::Block blk = kp->blocks[item];
+  UG_CHECK(blk.task >= 0 && blk.task < kp->n_tasks && blk.bh >= 0 && blk.bh < kp->n_bh, 0);
   const ug::Task task = kp->tasks[blk.task];
+  UG_CHECK(task.q0 >= 0 && task.q0 < task.q1 && task.q1 <= kp->L && task.q1 - task.q0 <= ug::kAttnQueryTile, 1);
   const int32_t b = blk.bh / kp->heads, h = blk.bh - b * kp->heads;
   const int64_t hoff = int64_t(b) * kp->batch_stride + int64_t(h) * D;
   const T* __restrict__ qg = static_cast<const T*>(kp->q) + hoff;
@@ -484,7 +491,12 @@ __device__ __forceinline__ void attn_item_f32(KArgs kp, int32_t item, char* smem
   // loop is an LDS read rather than a global load that would wait on the tile
   // loads in flight.
   const int32_t nr = task.r1 - task.r0;
-  if (tid < nr) s_rng[tid] = kp->ranges[task.r0 + tid];
+  UG_CHECK(nr >= 1 && nr <= ug::kAttnMaxRanges, 1);
+  if (tid < nr) {
+    const ug::Range r = kp->ranges[task.r0 + tid];
+    UG_CHECK(r.k0 >= 0 && r.k0 < r.k1 && r.k1 <= kp->L, 1);
+    s_rng[tid] = r;
+  }
 
   // The wave's queries as the B operand of S^T = K Q^T.
   constexpr int kQRegs = D / 2;
@@ -636,6 +648,7 @@ __device__ __forceinline__ void attn_item_f32(KArgs kp, int32_t item, char* smem
   kp = kernel_args();  // the epilogue's arguments are loaded here, not kept across the loop
   const float total = pair_sum(lsum);
   const float inv = 1.0f / total;
+  UG_CHECK(!(kp->lse && g == 0 && qrow < task.q1) || qrow < kp->lse_rows, 3);
   if (kp->lse && g == 0 && qrow < task.q1)  // log(sum_j exp(s_j)) = (m2 + log2(total)) * ln 2
     kp->lse[int64_t(blk.bh) * kp->lse_rows + qrow] = (m2 + __log2f(total)) * 0.6931471805599453f;
   char* const ost = smem + wave * 32 * RB;
@@ -677,8 +690,10 @@ __device__ __forceinline__ void attn_item_f32(KArgs kp, int32_t item, char* smem
     const int r = pass * rows_per_pass + lane / Lds::kChunks;
     const int cc = lane % Lds::kChunks;
     const uint4 val = *reinterpret_cast<const uint4*>(ost + r * RB + ((cc ^ Lds::k_swz(r)) * 16));
-    if (task.q0 + wave * 32 + r < task.q1)
+    if (task.q0 + wave * 32 + r < task.q1) {
+      UG_CHECK(orow[pass] >= 0 && orow[pass] < kp->L, 3);
       *reinterpret_cast<uint4*>(og + int64_t(orow[pass]) * rs + cc * Lds::kEl16) = val;
+    }
   }
 }
 
@@ -700,8 +715,11 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
   constexpr float kHeadroom = 8.0f;         // octaves between the reference and the largest weight seen
   static_assert(kSlots * kExpPerSlot == 32, "32 weights per lane and tile");
 
+  UG_CHECK(item >= 0 && item < kp->queue_len * ug::kXcds, 0);
   const ug::Block blk = kp->blocks[item];
+  UG_CHECK(blk.task >= 0 && blk.task < kp->n_tasks && blk.bh >= 0 && blk.bh < kp->n_bh, 0);
   const ug::Task task = kp->tasks[blk.task];
+  UG_CHECK(task.q0 >= 0 && task.q0 < task.q1 && task.q1 <= kp->L && task.q1 - task.q0 <= ug::kAttnQueryTile, 1);
   const int32_t b = blk.bh / kp->heads, h = blk.bh - b * kp->heads;
   const int64_t hoff = int64_t(b) * kp->batch_stride + int64_t(h) * D;
   const T* __restrict__ qg = static_cast<const T*>(kp->q) + hoff;
@@ -724,7 +742,12 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
   // LDS read rather than a global load that would wait on the tile loads in
   // flight.
   const int32_t nr = task.r1 - task.r0;
-  if (tid < nr) s_rng[tid] = kp->ranges[task.r0 + tid];
+  UG_CHECK(nr >= 1 && nr <= ug::kAttnMaxRanges, 1);
+  if (tid < nr) {
+    const ug::Range r = kp->ranges[task.r0 + tid];
+    UG_CHECK(r.k0 >= 0 && r.k0 < r.k1 && r.k1 <= kp->L, 1);
+    s_rng[tid] = r;
+  }
 
   // The wave's queries as the B operand of S^T = K Q^T.
   bf16x8 qf[kQRegs];
@@ -999,6 +1022,7 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
     pv_all(pa, smem + 2 * TB);
   const float total = pair_sum(lsum);
   const float inv = 1.0f / total;
+  UG_CHECK(!(kp->lse && g == 0 && qrow < task.q1) || qrow < kp->lse_rows, 3);
   if (kp->lse && g == 0 && qrow < task.q1)  // log(sum_j exp(s_j)) = (mref + log2(total)) * ln 2
     kp->lse[int64_t(blk.bh) * kp->lse_rows + qrow] = (mref + __log2f(total)) * 0.6931471805599453f;
   __syncthreads();  // every wave has read the last V tile before the staging below overwrites it
@@ -1033,8 +1057,10 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
     const int r = pass * rows_per_pass + lane / Lds::kChunks;
     const int cc = lane % Lds::kChunks;
     const uint4 val = *reinterpret_cast<const uint4*>(ost + r * RB + ((cc ^ Lds::k_swz(r)) * 16));
-    if (task.q0 + wave * 32 + r < task.q1)
+    if (task.q0 + wave * 32 + r < task.q1) {
+      UG_CHECK(orow[pass] >= 0 && orow[pass] < kp->L, 3);
       *reinterpret_cast<uint4*>(og + int64_t(orow[pass]) * rs + cc * Lds::kEl16) = val;
+    }
   }
 }
 
@@ -1147,6 +1173,9 @@ ug_status attn_common(ug_plan_t p, const void* q, const void* k, const void* v, 
   ap.lse = lse;
   ap.lse_rows = p->L;
   ap.queue_len = int32_t(p->blocks.size() / ug::kXcds);
+  ap.L = int32_t(p->L);
+  ap.n_tasks = int32_t(p->tasks.size());
+  ap.n_bh = p->d.batch * p->d.heads;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = p->d.dtype == UG_BF16;
   return ug::launch_with_slot(p, s, fn, [&](int32_t* cursors) {
@@ -1287,3 +1316,5 @@ ug_status ug_permute_rope_bwd(ug_plan_t p, const void* dq_perm, const void* dk_p
 }
 
 }  // extern "C"
+
+UG_BOUNDS_ACCESSOR(ug_debug_bounds_fwd)

@@ -163,11 +163,13 @@ __global__ __launch_bounds__(kWarmThreads) void warm_start_kernel(const T* __res
 #pragma unroll
   // Every tap with a nonzero weight lies in the staged patch; a third tap
   // that does not (zero weight) is clamped into it, so it reads a staged
-  // (finite) sample rather than whatever the LDS held before.
-  for (int j = 0; j < 3; ++j) lxo[j] = (min(ax.base + j, x_hi) - x_lo) * nv + v;
+  // (finite) sample rather than whatever the LDS held before.  Threads past
+  // the block's vectors (nothing to store) read the last staged vector.
+  for (int j = 0; j < 3; ++j) lxo[j] = (min(ax.base + j, x_hi) - x_lo) * nv + min(v, nv - 1);
   // column passes of LR row y (clamped into the patch) into hc, hb
   auto column_pass = [&](int32_t y, float (&hc)[E], float (&hb)[E]) {
     const int32_t lrow = (min(y, y_hi) - y_lo) * nx * nv;
+    UG_CHECK(lrow >= 0 && lrow + lxo[0] < ny * nx * nv && lrow + lxo[2] < ny * nx * nv && lxo[0] >= 0, 5);
 #pragma unroll
     for (int e = 0; e < E; ++e) hc[e] = hb[e] = 0.f;
 #pragma unroll
@@ -223,6 +225,7 @@ __global__ __launch_bounds__(kWarmThreads) void warm_start_kernel(const T* __res
       for (int e = 0; e < E; ++e) o[e] = __bf16(o32[e]);
       out = *reinterpret_cast<u32x4*>(&o);
     }
+    UG_CHECK(!(col_ok && r0 + k < H) || (g0 + k * row_step >= 0 && g0 + k * row_step < int64_t(H) * W * vpp), 5);
     if (col_ok && r0 + k < H) __builtin_nontemporal_store(out, outv + g0 + k * row_step);
   }
 }
@@ -277,3 +280,5 @@ ug_status ug_warm_start(const ug_warm_desc* d, const void* x_lr, const void* noi
 }
 
 }  // extern "C"
+
+UG_BOUNDS_ACCESSOR(ug_debug_bounds_warm)

@@ -29,6 +29,22 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def test_debug_library_exports_its_symbols():
+    """The bounds-checking build exports the calls include/ultragen_debug.h
+    declares, besides every release entry point; the release build does not."""
+    with open(os.path.join(ROOT, "include", "ultragen_debug.h")) as f:
+        names = sorted(set(re.findall(r"^\s*ug_status\s+(ug_\w+)\s*\(", f.read(), re.M)))
+    assert set(names) == set(U.DEBUG_EXPORTED), names
+    if not os.path.exists(U.DEBUG_LIB_PATH):
+        pytest.skip("libultragen_debug.so is not built")
+    dbg = ctypes.CDLL(U.DEBUG_LIB_PATH)
+    for n in names + header_functions():
+        assert hasattr(dbg, n), n
+    rel = ctypes.CDLL(U.LIB_PATH)
+    for n in names:
+        assert not hasattr(rel, n), n
+
+
 def test_status_strings():
     assert U.ug_status_str(0) == "UG_OK"
     assert U.ug_status_str(1) == "UG_ERR_INVALID_ARGUMENT"
