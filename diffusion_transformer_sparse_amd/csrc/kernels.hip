@@ -425,6 +425,10 @@ struct TileLoader {
       load_lds<16>(base, off[i], (lds_void*)(tile + (i * kAttnThreads + wave * 64) * 16), bytes);
     (void)tid;
   }
+  // The thread's i-th 16-byte load of the tile at `base` (bytes as above).
+  __device__ __forceinline__ void issue_one(int i, const char* base, int32_t bytes, char* tile, int wave) const {
+    load_lds<16>(base, off[i], (lds_void*)(tile + (i * kAttnThreads + wave * 64) * 16), bytes);
+  }
 };
 
 // S^T (two 32-key blocks) = K Q^T for one 64-key tile in LDS.  koff[i] is
@@ -831,10 +835,20 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
       p[k >> 3][(k & 7) - 1] = pr[0];
       p[k >> 3][k & 7] = pr[1];
       // the row sum takes the rounded weights, the ones that multiply V (a
-      // dominant weight's rounding then cancels in the normalisation); a
-      // bf16 half moved into the high half of a word is that fp32 value
-      const uint32_t u = __builtin_bit_cast(uint32_t, pr);
-      d += __uint_as_float(u << 16) + __uint_as_float(u & 0xffff0000u);
+      // dominant weight's rounding then cancels in the normalisation).  At
+      // head_dim 128 the pair is split into two fp32 values by two bit
+      // operations (a bf16 half moved into the high half of a word is that
+      // value) and added; at head_dim 64, where the step has half as many
+      // MFMAs to hide VALU work behind, one dot product with (1, 1) adds it.
+      // The first pair starts the sum (d enters as 0).
+      if constexpr (D == 64) {
+        const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
+        d = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, k == 1 ? 0.0f : d, false);
+      } else {
+        const uint32_t u = __builtin_bit_cast(uint32_t, pr);
+        const float x = __uint_as_float(u << 16) + __uint_as_float(u & 0xffff0000u);
+        d = k == 1 ? x : d + x;
+      }
       asm volatile("" : "+v"(d));
     }
   };
@@ -935,7 +949,33 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
     const char* const v_prev = smem + 2 * TB + (PAR ? 0 : TB);  // V_{i-1}
     const int32_t nv_s = nv_pend;                               // rows of tile i+1
     const bool has_s = i + 1 < ntiles;
-    nv_pend = issue_loads(i, PAR);
+    // The step's loads (K_{i+2} and V_i, as issue_loads) go out one at a time,
+    // kLoadGap slots apart, after the first operand reads rather than all
+    // before them, where the eight waves' loads and those reads would meet.
+    // With no K_{i+2} the K loads read zero bytes (into the slot K_i left).
+    const char* kbase = reinterpret_cast<const char*>(kg);
+    int32_t kbytes = 0;
+    nv_pend = kKT;
+    if (i + 2 < ntiles) {
+      nv_pend = ck.nv();
+      kbase = reinterpret_cast<const char*>(kg + int64_t(ck.ks) * rs);
+      kbytes = __builtin_amdgcn_readfirstlane(nv_pend * int32_t(rs) * int32_t(sizeof(T)));  // nv_pend >= 1
+      ck.advance(s_rng);
+    }
+    const char* const vbase = reinterpret_cast<const char*>(vg + int64_t(cv.ks) * rs);
+    // V_i exists (i < ntiles), so it has at least one row
+    const int32_t vbytes = __builtin_amdgcn_readfirstlane(cv.nv() * int32_t(rs) * int32_t(sizeof(T)));
+    cv.advance(s_rng);
+    constexpr int kLPT = Lds::kLoadsPerThread;
+    constexpr int kLoadGap = D == 64 ? 4 : 2;
+    static_assert(kLoadGap * 2 * kLPT <= kSlots, "the loads fit in the step");
+    auto load_at = [&](int k) {
+      if (k % kLoadGap == 0 && k / kLoadGap < 2 * kLPT) {
+        const int j = k / kLoadGap;
+        if ((j & 1) == 0) kld.issue_one(j >> 1, kbase, kbytes, smem + (PAR ? TB : 0), wave);
+        else vld.issue_one(j >> 1, vbase, vbytes, smem + 2 * TB + (PAR ? TB : 0), wave);
+      }
+    };
     bf16x8 opnd[kLead + 1];  // operand ring: slot k's A operand in opnd[k % (kLead + 1)]
     auto fetch = [&](int k) {
       const int j = k >> 1;
@@ -954,6 +994,7 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
     float d = 0.f;
 #pragma unroll
     for (int k = 0; k < kSlots; ++k) {
+      load_at(k);
       if (k + kLead < kSlots) fetch(k + kLead);
       const int j = k >> 1;
       if ((k & 1) == 0) {
@@ -968,7 +1009,7 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
       for (int e = 0; e < kExpPerSlot; ++e) weight(s_cur, p_nxt, d, k * kExpPerSlot + e);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (__builtin_amdgcn_readfirstlane(int(has_s && nv_s < kKT))) mask_tail(s_nxt, nv_s);
+    if (has_s && nv_s < kKT) mask_tail(s_nxt, nv_s);  // uniform (scalar) condition
     if (__ballot(!(d < 256.0f))) settle(s_cur, p_nxt, d);
     lsum += d;
     __builtin_amdgcn_s_waitcnt(0);  // this thread's direct-to-LDS loads have landed
