@@ -684,9 +684,15 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
   store_block<D>(dva, 1.0f, ost, p.dv + hoff, rs, task.q0 + wave * 32, task.q1, lane);
 }
 
+// prep on `s`; then the dQ pass on `s` and the dK/dV pass on the plan's
+// second stream side by side (each fills the compute units the other's tail
+// leaves idle; they read the same inputs and write different outputs), and
+// `s` waits for both.  Stream capture is refused before anything is queued.
 template <int D>
 ug_status launch_bwd(ug_plan_t p, BwdParams bp, const __bf16* o, const float* lse, float* lse2, float* delta,
                      hipStream_t s, const char* fn) {
+  ug_status st = ug::refuse_capture(s, fn);
+  if (st != UG_OK) return st;
   const int32_t Lp = int32_t(p->stat_rows());
   const int32_t units = std::min(p->d.heads, kPrepHeads) * (D / 8);
   const unsigned prep_threads = unsigned(std::min(1024, (units + 63) / 64 * 64));
@@ -694,31 +700,45 @@ ug_status launch_bwd(ug_plan_t p, BwdParams bp, const __bf16* o, const float* ls
                      dim3(unsigned((Lp + kPrepRows - 1) / kPrepRows), unsigned(p->d.batch),
                           unsigned((p->d.heads + kPrepHeads - 1) / kPrepHeads)),
                      dim3(prep_threads), 0, s, o, bp.d_o, lse, lse2, delta, int32_t(p->L), Lp, p->d.heads);
+  bp.L = int32_t(p->L);
+  bp.n_bh = p->d.batch * p->d.heads;
+  BwdParams kq = bp;  // the dK/dV pass: the transposed (key-major) tables
+  kq.tasks = p->d_ktasks;
+  kq.ranges = p->d_kranges;
+  kq.blocks = p->d_kblocks;
+  kq.n_tasks = int32_t(p->ktasks.size());
+  kq.mask_off = p->d_kmask_off;
+  kq.masks = p->d_kmasks;
   bp.tasks = p->d_tasks;
   bp.ranges = p->d_ranges;
   bp.blocks = p->d_blocks;
-  bp.L = int32_t(p->L);
   bp.n_tasks = int32_t(p->tasks.size());
-  bp.n_bh = p->d.batch * p->d.heads;
+
+  std::lock_guard<std::mutex> lock(p->bwd_mu);
+  auto hip_fail = [&](const char* what) {
+    return ug::fail(UG_ERR_HIP, std::string(fn) + ": " + what + " failed: " + hipGetErrorString(hipGetLastError()));
+  };
+  if (hipEventRecord(p->bwd_fork, s) != hipSuccess) return hip_fail("hipEventRecord");
+  if (hipStreamWaitEvent(p->bwd_aux, p->bwd_fork, 0) != hipSuccess) return hip_fail("hipStreamWaitEvent");
   if (!p->blocks.empty()) {
     bp.queue_len = int32_t(p->blocks.size() / ug::kXcds);
     const unsigned grid = unsigned(std::min<size_t>(size_t(p->cus), p->blocks.size()));
-    const ug_status st = ug::launch_with_slot(p, s, fn, [&](int32_t* cursors) {
+    st = ug::launch_with_slot(p, s, fn, [&](int32_t* cursors) {
       bp.queue = cursors;
       hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3(grid), dim3(kThreads), 0, s, bp);
       return launch_status(fn);
     });
-    if (st != UG_OK) return st;
   }
-  bp.tasks = p->d_ktasks;
-  bp.ranges = p->d_kranges;
-  bp.blocks = p->d_kblocks;
-  bp.n_tasks = int32_t(p->ktasks.size());
-  bp.mask_off = p->d_kmask_off;
-  bp.masks = p->d_kmasks;
-  if (!p->kblocks.empty())
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3(unsigned(p->kblocks.size())), dim3(kThreads), 0, s, bp);
-  return launch_status(fn);
+  if (st == UG_OK && !p->kblocks.empty()) {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3(unsigned(p->kblocks.size())), dim3(kThreads), 0, p->bwd_aux,
+                       kq);
+    st = launch_status(fn);
+  }
+  // the join is queued whatever happened above, so `s` never runs ahead of
+  // work already queued on the second stream
+  if (hipEventRecord(p->bwd_join, p->bwd_aux) != hipSuccess) return hip_fail("hipEventRecord");
+  if (hipStreamWaitEvent(s, p->bwd_join, 0) != hipSuccess) return hip_fail("hipStreamWaitEvent");
+  return st;
 }
 
 // Scratch of ug_attn_bwd_noalloc: the per-row statistics (log2 LSE and

@@ -18,6 +18,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 #include <numeric>
 #include <stdexcept>
@@ -507,6 +508,12 @@ void free_device(ug_plan_s* p) {
     if (e) (void)hipEventDestroy(e);
     e = nullptr;
   }
+  for (hipEvent_t* e : {&p->bwd_fork, &p->bwd_join}) {
+    if (*e) (void)hipEventDestroy(*e);
+    *e = nullptr;
+  }
+  if (p->bwd_aux) (void)hipStreamDestroy(p->bwd_aux);
+  p->bwd_aux = nullptr;
   p->d_perm = p->d_inv = nullptr;
   p->d_lr_perm = p->d_lr_inv = nullptr;
   p->d_rope = nullptr;
@@ -554,6 +561,18 @@ ug_status alloc_queue(ug_plan_s* p) {
   for (hipEvent_t& e : p->slot_events)
     if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
       e = nullptr;
+      return fail(UG_ERR_HIP, std::string("ug_plan: hipEventCreateWithFlags failed: ") +
+                                  hipGetErrorString(hipGetLastError()));
+    }
+  // the backward's second stream (default priority) and its fork / join events
+  if (hipStreamCreateWithFlags(&p->bwd_aux, hipStreamNonBlocking) != hipSuccess) {
+    p->bwd_aux = nullptr;
+    return fail(UG_ERR_HIP, std::string("ug_plan: hipStreamCreateWithFlags failed: ") +
+                                hipGetErrorString(hipGetLastError()));
+  }
+  for (hipEvent_t* e : {&p->bwd_fork, &p->bwd_join})
+    if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess) {
+      *e = nullptr;
       return fail(UG_ERR_HIP, std::string("ug_plan: hipEventCreateWithFlags failed: ") +
                                   hipGetErrorString(hipGetLastError()));
     }

@@ -110,6 +110,14 @@ struct ug_plan_s {
   std::mutex launch_mu;
   ug::SlotRing<ug::kQueueSlots> slots;
   hipEvent_t slot_events[ug::kQueueSlots] = {};
+
+  // The backward's second stream: its dK/dV pass runs there, beside the dQ
+  // pass on the caller's stream, between a fork and a join event; `bwd_mu`
+  // keeps each call's record / wait / launch sequence whole.
+  std::mutex bwd_mu;
+  hipStream_t bwd_aux = nullptr;
+  hipEvent_t bwd_fork = nullptr;
+  hipEvent_t bwd_join = nullptr;
 };
 
 namespace ug {
@@ -122,8 +130,9 @@ void clear_error();
 // share it with every replay), takes the next slot, makes the stream wait
 // for the slot's previous launch, runs `launch(cursors)` and records the
 // slot's event after it.  Returns UG_OK or a failure already reported.
-template <typename F>
-ug_status launch_with_slot(ug_plan_s* p, hipStream_t s, const char* fn, F&& launch) {
+// UG_OK unless `s` is capturing (refused: a captured persistent launch would
+// take its cursor slot at capture time and share it with every replay).
+inline ug_status refuse_capture(hipStream_t s, const char* fn) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
     (void)hipGetLastError();
@@ -132,6 +141,13 @@ ug_status launch_with_slot(ug_plan_s* p, hipStream_t s, const char* fn, F&& laun
   if (cs != hipStreamCaptureStatusNone)
     return fail(UG_ERR_UNSUPPORTED, std::string(fn) + ": stream capture is not supported (each launch takes a "
                                                       "work-queue cursor slot at launch time)");
+  return UG_OK;
+}
+
+template <typename F>
+ug_status launch_with_slot(ug_plan_s* p, hipStream_t s, const char* fn, F&& launch) {
+  const ug_status cap = refuse_capture(s, fn);
+  if (cap != UG_OK) return cap;
   std::lock_guard<std::mutex> lock(p->launch_mu);
   const auto t = p->slots.take();
   if (t.reused && hipStreamWaitEvent(s, p->slot_events[t.slot], 0) != hipSuccess)

@@ -84,14 +84,15 @@ __device__ __forceinline__ void load_f32(const T* p, float (&x)[16 / sizeof(T)])
 //   Hc[m] = sum_j wc_x[j] X[m][x0+j],  Hb[m] = sum_j wb_x[j] X[m][x0+j]
 // (the column passes of LR row m), the pixel's value is
 //   sum_i (1 + s) wc_y[i] Hc[y0+i] - s wb_y[i] Hb[y0+i].
-// A thread keeps the column passes of three consecutive LR rows in
+// The row weights also carry the blend's factor 1 - alpha, so the output is
+// one more FMA with alpha and the noise.  A thread keeps the column passes of three consecutive LR rows in
 // registers and slides them down as the tile's rows move to the next LR
 // row, so each LR sample is converted and weighted once per thread.
 constexpr int kTileH = 8, kVecBlock = 8, kTileW = kWarmThreads / kVecBlock;
 
 __host__ __device__ constexpr int lr_span(int tile, int rho) { return (tile + 1) / rho + 3; }
 
-struct RowWeights {  // one HR row: LR rows base .. base+2 with (1 + s) wc and s wb
+struct RowWeights {  // one HR row: LR rows base .. base+2 with (1 - alpha)(1 + s) wc and (1 - alpha) s wb
   int base;
   float ca[3], cb[3];
 };
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(kWarmThreads) void warm_start_kernel(const T* __res
     RowWeights rw;
     rw.base = a.base;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) rw.ca[i] = (1.f + s) * a.wc[i], rw.cb[i] = s * a.wb[i];
+    for (int i = 0; i < 3; ++i) rw.ca[i] = (1.f - alpha) * (1.f + s) * a.wc[i], rw.cb[i] = (1.f - alpha) * s * a.wb[i];
     s_ay[tid] = rw;
   }
   if (tid >= 64 && tid < 64 + kTileW) s_ax[tid - 64] = axis_weights(min(c0 + tid - 64, W - 1), W, w, rho);
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(kWarmThreads) void warm_start_kernel(const T* __res
       acc = fmaf(-ay.cb[0], hb[0][e], acc);
       acc = fmaf(-ay.cb[1], hb[1][e], acc);
       acc = fmaf(-ay.cb[2], hb[2][e], acc);
-      o32[e] = alpha * nf[e] + (1.f - alpha) * acc;
+      o32[e] = fmaf(alpha, nf[e], acc);  // acc carries the factor 1 - alpha
     }
     u32x4 out;
     if constexpr (std::is_same<T, float>::value) {

@@ -140,7 +140,8 @@ typedef struct ug_plan_s* ug_plan_t;
  * range list and workgroup order, RoPE cos/sin table computed in double and
  * stored as float) and, unless UG_PLAN_HOST_ONLY, upload them to the current
  * HIP device and allocate the attention's zeroed work-queue cursors (4 KiB)
- * there (synchronous).  The window-first order is 关键设计 1's regrouping
+ * there, with the events that order their reuse and the backward's second
+ * stream (synchronous).  The window-first order is 关键设计 1's regrouping
  * of tokens window by window; the neighbourhood is its adjacent-window
  * interaction.  On success *out owns everything; free it with ug_plan_free
  * once no launched work still uses it.
@@ -293,7 +294,12 @@ ug_status ug_attn_fwd_raster(ug_plan_t plan, const void* q, const void* k, const
  * written in full (no accumulation into them) and must not overlap each
  * other, the inputs, lse or the workspace.  The result does not depend on
  * scheduling (no atomics).  Products in bf16 MFMA with fp32 accumulation;
- * P and dS are rounded to bf16 as MFMA operands.
+ * P and dS are rounded to bf16 as MFMA operands.  The dK/dV pass runs on a
+ * stream the plan owns, beside the dQ pass on `stream`, forked from and
+ * joined back to `stream` by events: work queued on `stream` afterwards sees
+ * all three gradients, as with a single stream.  Calls on one plan from
+ * several host threads are serialised while they queue their work; stream
+ * capture is refused (UG_ERR_UNSUPPORTED) before anything is queued.
  *
  * ug_rope2d_bwd: in place on permuted dq and dk, the transpose of
  * ug_rope2d's rotation (each pair turns by the negated angle), which maps

@@ -251,6 +251,58 @@ def test_backward_is_deterministic(U):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+def test_backward_on_two_streams_at_once(U):
+    """ug_attn_bwd runs its dK/dV pass on a stream of the plan's, forked from
+    and joined back to the caller's stream: two calls on one plan from two
+    streams at once give the one-stream gradients bit for bit, and copies
+    queued on each caller's stream right after its call see all three."""
+    import torch
+    w = WL.WORKLOADS["1k"]
+    p = U.ug_plan(U.desc_of(w))
+    q, k, v, do = inputs(w)
+    o, lse = U.ug_attn_fwd_lse(p, q, k, v)
+    ref = U.ug_attn_bwd(p, q, k, v, o, do, lse)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    grads, copies = [], []
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            g = U.ug_attn_bwd(p, q, k, v, o, do, lse)
+            copies.append([t.clone() for t in g])  # queued on s after the call
+            grads.append(g)
+    torch.cuda.synchronize()
+    for i in range(2):
+        for name, got, cp, r in zip(("dq", "dk", "dv"), grads[i], copies[i], ref):
+            assert torch.equal(got.view(torch.int16), r.view(torch.int16)), f"stream {i} {name}"
+            assert torch.equal(cp.view(torch.int16), r.view(torch.int16)), f"stream {i} {name} (copy)"
+
+
+def test_backward_refuses_stream_capture(U):
+    """The backward's dQ pass takes a work-queue cursor slot at launch time,
+    so the call refuses stream capture with UG_ERR_UNSUPPORTED before it
+    queues anything, and the plan works as before afterwards."""
+    import torch
+    w = WL.WORKLOADS["small_ragged"]
+    p = U.ug_plan(U.desc_of(w))
+    q, k, v, do = inputs(w)
+    o, lse = U.ug_attn_fwd_lse(p, q, k, v)
+    ref = U.ug_attn_bwd(p, q, k, v, o, do, lse)
+    outs = [torch.empty_like(q) for _ in range(3)]
+    ws = U.bwd_workspace(p, q.device)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(U.UgError) as err:
+        with torch.cuda.graph(g):
+            U.ug_attn_bwd(p, q, k, v, o, do, lse, *outs, workspace=ws)
+    assert err.value.status == 2  # UG_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    again = U.ug_attn_bwd(p, q, k, v, o, do, lse, *outs, workspace=ws)
+    torch.cuda.synchronize()
+    for x, r in zip(again, ref):
+        assert torch.equal(x.view(torch.int16), r.view(torch.int16))
+
+
 def test_full_size_backward_whole_head(U):
     """The 4K layer's backward: dq, dk and dv of every row of one head
     (text, HR and LR queries and keys) against the oracle's whole-head
