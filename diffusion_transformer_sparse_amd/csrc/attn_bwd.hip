@@ -134,7 +134,6 @@ struct LaneOffsets {
 // c (32 tile rows 32mb .. 32mb+31 x 32 register columns) = sum over the D
 // dims of tile[row][dim] * b[column][dim]; b[i] holds dims 16i + 8g .. +7 of
 // the lane's column.  Output lane l: column l%32, rows 8*(j/4) + 4g + j%4.
-// rows_x_rows is the same with the columns read from a 32-row LDS block.
 template <int D>
 __device__ __forceinline__ f32x16 rows_x_regs(const char* tile, int mb, const bf16x8 (&b)[D / 16],
                                               const LaneOffsets<D>& lo) {
@@ -144,17 +143,6 @@ __device__ __forceinline__ f32x16 rows_x_regs(const char* tile, int mb, const bf
 #pragma unroll
   for (int i = 1; i < D / 16; ++i)
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(t0 + lo.row[i]), b[i], c, 0, 0, 0);
-  return c;
-}
-
-template <int D>
-__device__ __forceinline__ f32x16 rows_x_rows(const char* tile, int mb, const char* cols, const LaneOffsets<D>& lo) {
-  const char* t0 = tile + mb * 32 * Tile<D>::RB;
-  f32x16 c = f32x16{};
-#pragma unroll
-  for (int i = 0; i < D / 16; ++i)
-    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(t0 + lo.row[i]),
-                                                *reinterpret_cast<const bf16x8*>(cols + lo.row[i]), c, 0, 0, 0);
   return c;
 }
 
@@ -555,7 +543,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int32_t b = blk.bh / p.heads, h = blk.bh - b * p.heads;
   const int64_t hoff = int64_t(b) * p.batch_stride + int64_t(h) * D;
   const int64_t rs = p.row_stride;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave index in a scalar register, masked so that alias analysis keeps its range
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (kThreads / 64 - 1);
   const int l32 = lane & 31, g = lane >> 5;
   const int32_t krow = task.q0 + wave * 32 + l32;
   const int32_t kload = min(krow, task.q1 - 1);
@@ -638,13 +628,43 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       if (seen == 0) break;  // no key of this wave sees the range (uniform)
-      const f32x16 s = rows_x_regs<D>(qt, mb, kf, lo);
-      const f32x16 dp = rows_x_rows<D>(dot, mb, vblk, lo);
-      // one 16-query chunk (registers 8cc .. 8cc+7) at a time: P and dS of
-      // the chunk, then its eight MFMAs
+      // S = Q K^T (B: K in registers) and dP = dO V^T (B: the wave's V rows)
+      // as alternating MFMAs, their LDS operands kSLead slots ahead
+      f32x16 s = f32x16{}, dp = f32x16{};
+      {
+        constexpr int kS = 2 * (D / 16);
+        constexpr int kSLead = 1;
+        bf16x8 oa[kSLead + 1], ob[kSLead + 1];
+        const char* q0 = qt + mb * 32 * L::RB;
+        const char* d0 = dot + mb * 32 * L::RB;
+        auto sfetch = [&](int k) {
+          const int i = k >> 1;
+          if ((k & 1) == 0) {
+            oa[k % (kSLead + 1)] = *reinterpret_cast<const bf16x8*>(q0 + lo.row[i]);
+          } else {
+            oa[k % (kSLead + 1)] = *reinterpret_cast<const bf16x8*>(d0 + lo.row[i]);
+            ob[k % (kSLead + 1)] = *reinterpret_cast<const bf16x8*>(vblk + lo.row[i]);
+          }
+        };
+#pragma unroll
+        for (int k = 0; k < kSLead; ++k) sfetch(k);
+#pragma unroll
+        for (int k = 0; k < kS; ++k) {
+          if (k + kSLead < kS) sfetch(k + kSLead);
+          const int i = k >> 1;
+          if ((k & 1) == 0)
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[k % (kSLead + 1)], kf[i], s, 0, 0, 0);
+          else
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[k % (kSLead + 1)], ob[k % (kSLead + 1)], dp, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // P and dS of both 16-query chunks (registers 8cc .. 8cc+7) first, so
+      // that S and dP are dead during the 16 MFMAs, whose operands then run
+      // kLead reads ahead through a register ring
+      bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        bf16x8 pb, dsb;
 #pragma unroll
         for (int a2 = 0; a2 < 2; ++a2) {
           const int a = 2 * cc + a2;
@@ -658,20 +678,29 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv_kernel(BwdParams p) {
             const int j = 4 * a + e;
             float pv = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(fmaf(s[j], c2, -lv[e])), 0.f, 1.f);
             if (!all_see && !sees) pv = 0.f;
-            pb[4 * a2 + e] = __bf16(pv);
-            dsb[4 * a2 + e] = __bf16(pv * (dp[j] - dl[e]));
+            pb[cc][4 * a2 + e] = __bf16(pv);
+            dsb[cc][4 * a2 + e] = __bf16(pv * (dp[j] - dl[e]));
           }
         }
+      }
+      constexpr int kM = 4 * (D / 32);  // MFMAs: 2 chunks x D/32 dim tiles x (dV, dK)
+      constexpr int kLead = 2;
+      bf16x8 opnd[kLead + 1];
+      auto fetch = [&](int k) {  // k = (cc * D/32 + t) * 2 + (0: dV from dO, 1: dK from Q)
+        const int cc = k / (2 * (D / 32)), t = (k / 2) % (D / 32);
+        opnd[k % (kLead + 1)] = tr_operand<D>((k & 1) ? qt : dot, t, 2 * mb + cc, lo);
+      };
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          dva[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(dot, t, 2 * mb + cc, lo), pb, dva[t], 0, 0, 0);
-          dka[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qt, t, 2 * mb + cc, lo), dsb, dka[t], 0, 0, 0);
-        }
+      for (int k = 0; k < kLead; ++k) fetch(k);
 #pragma unroll
-        for (int k = 0; k < 2 * (D / 32); ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        }
+      for (int k = 0; k < kM; ++k) {
+        if (k + kLead < kM) fetch(k + kLead);
+        const int cc = k / (2 * (D / 32)), t = (k / 2) % (D / 32);
+        if ((k & 1) == 0)
+          dva[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[k % (kLead + 1)], pb[cc], dva[t], 0, 0, 0);
+        else
+          dka[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[k % (kLead + 1)], dsb[cc], dka[t], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     nv = nv_next;
