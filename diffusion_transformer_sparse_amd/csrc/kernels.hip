@@ -824,37 +824,55 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
   // volatile asm statements pin the work to its slot: without them the
   // compiler gathers it after the MFMAs, where nothing hides it.
   float e_hold = 0.f;
+  bf16x2 pr_prev = {};  // the last packed pair, whose row-sum term is still to be added
+  // The row sum takes the rounded weights, the ones that multiply V (a
+  // dominant weight's rounding then cancels in the normalisation).  At
+  // head_dim 128 a pair is split into two fp32 values by two bit operations
+  // (a bf16 half moved into the high half of a word is that value) and
+  // added; at head_dim 64, where the step has half as many MFMAs to hide
+  // VALU work behind, one dot product with (1, 1) adds it, one pair late:
+  // between the next pair's exponential and its pack, where it fills the
+  // wait states those two would need (at head_dim 128 those waits are hidden
+  // behind the MFMAs and the late order measured slower).  `first` starts
+  // the sum (d enters as 0).
+  constexpr bool kLateSum = D == 64;
+  auto sum_pair = [&](float& d, bf16x2 pr, bool first) {
+    if constexpr (D == 64) {
+      const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
+      d = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, first ? 0.0f : d, false);
+    } else {
+      const uint32_t u = __builtin_bit_cast(uint32_t, pr);
+      const float x = __uint_as_float(u << 16) + __uint_as_float(u & 0xffff0000u);
+      d = first ? x : d + x;
+    }
+    asm volatile("" : "+v"(d));
+  };
   auto weight = [&](const f32x16(&s)[2], bf16x8(&p)[4], float& d, int k) {
-    const float e = __builtin_amdgcn_exp2f(fmaf(s[k >> 4][k & 15], c2, -mref));
+    float e = __builtin_amdgcn_exp2f(fmaf(s[k >> 4][k & 15], c2, -mref));
     if ((k & 1) == 0) {
       e_hold = e;
       asm volatile("" : "+v"(e_hold));
     } else {
+      if constexpr (kLateSum) {
+        asm volatile("" : "+v"(e));
+        if (k >= 3) sum_pair(d, pr_prev, k == 3);
+      }
       bf16x2 pr = {__bf16(e_hold), __bf16(e)};
       asm volatile("" : "+v"(pr));
       p[k >> 3][(k & 7) - 1] = pr[0];
       p[k >> 3][k & 7] = pr[1];
-      // the row sum takes the rounded weights, the ones that multiply V (a
-      // dominant weight's rounding then cancels in the normalisation).  At
-      // head_dim 128 the pair is split into two fp32 values by two bit
-      // operations (a bf16 half moved into the high half of a word is that
-      // value) and added; at head_dim 64, where the step has half as many
-      // MFMAs to hide VALU work behind, one dot product with (1, 1) adds it.
-      // The first pair starts the sum (d enters as 0).
-      if constexpr (D == 64) {
-        const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
-        d = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, k == 1 ? 0.0f : d, false);
-      } else {
-        const uint32_t u = __builtin_bit_cast(uint32_t, pr);
-        const float x = __uint_as_float(u << 16) + __uint_as_float(u & 0xffff0000u);
-        d = k == 1 ? x : d + x;
-      }
-      asm volatile("" : "+v"(d));
+      if constexpr (kLateSum) pr_prev = pr;
+      else sum_pair(d, pr, k == 1);
     }
+  };
+  // the last pair's term, once all 32 weights of a tile are formed
+  auto sum_last = [&](float& d) {
+    if constexpr (kLateSum) sum_pair(d, pr_prev, false);
   };
   auto weights_all = [&](const f32x16(&s)[2], bf16x8(&p)[4], float& d) {
 #pragma unroll
     for (int k = 0; k < 32; ++k) weight(s, p, d, k);
+    sum_last(d);
   };
   // Some lane's weights of tile s may be large: move the reference up by a
   // whole number of octaves, to kHeadroom above the tile's maximum, rescale
@@ -1009,6 +1027,7 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
       for (int e = 0; e < kExpPerSlot; ++e) weight(s_cur, p_nxt, d, k * kExpPerSlot + e);
       __builtin_amdgcn_sched_barrier(0);
     }
+    sum_last(d);
     if (has_s && nv_s < kKT) mask_tail(s_nxt, nv_s);  // uniform (scalar) condition
     if (__ballot(!(d < 256.0f))) settle(s_cur, p_nxt, d);
     lsum += d;
