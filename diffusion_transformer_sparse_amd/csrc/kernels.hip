@@ -968,9 +968,9 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
     const int32_t nv_s = nv_pend;                               // rows of tile i+1
     const bool has_s = i + 1 < ntiles;
     // The step's loads (K_{i+2} and V_i, as issue_loads) go out one at a time,
-    // kLoadGap slots apart, after the first operand reads rather than all
-    // before them, where the eight waves' loads and those reads would meet.
-    // With no K_{i+2} the K loads read zero bytes (into the slot K_i left).
+    // kLoadGap slots apart, rather than all at the step's start, where the
+    // eight waves' loads and their first operand reads would meet.  With no
+    // K_{i+2} the K loads read zero bytes (into the slot K_i left).
     const char* kbase = reinterpret_cast<const char*>(kg);
     int32_t kbytes = 0;
     nv_pend = kKT;
