@@ -10,7 +10,10 @@ is compared with oracle.allowed_keys_of, and the union of a key row's
 rows are mapped to raster rows with the oracle's own window-first orders.
 Both oracle functions depend on a row only through its coordinates class
 (kind, window): every row is checked, the oracle set is computed once per
-class."""
+class.  Besides the evaluation workloads and hand-picked radius 2 and 4
+cases, 96 seeded random small geometries (windows of 2 to 16, radius 0 to
+3, rho 1 to 5, default, explicit or no LR grid, both LR modes) are checked
+the same way."""
 import numpy as np
 import pytest
 
@@ -26,6 +29,34 @@ EXTRA = {
     "radius2_corr_ragged": dict(hr_h=100, hr_w=70, lr_h=25, lr_w=18, n_text=8, radius=2, lr_mode=1),
     "no_text_no_lr": dict(hr_h=48, hr_w=40, lr_h=0, lr_w=0, n_text=0, radius=1),
 }
+
+
+
+def _random_cases(n=96):
+    """Seeded small geometries beyond the hand-picked ones: odd grids, windows
+    of 2 to 16, radius 0 to 3, text 0 to 37 rows, rho 1 to 5, the default,
+    an explicit (possibly overhanging or short) or no LR grid, both LR modes."""
+    rng = np.random.default_rng([2026, 77])
+    out = {}
+    for i in range(n):
+        H, W = int(rng.integers(1, 71)), int(rng.integers(1, 71))
+        rho = int(rng.integers(1, 6))
+        kind = int(rng.integers(0, 3))
+        if kind == 0:
+            lh = lw = None
+        elif kind == 1:
+            lh = lw = 0
+        else:
+            lh = int(rng.integers(1, -(-H // rho) + 4))
+            lw = int(rng.integers(1, -(-W // rho) + 4))
+        out[f"random{i:02d}"] = dict(hr_h=H, hr_w=W, lr_h=lh, lr_w=lw, n_text=int(rng.choice([0, 1, 5, 37])),
+                                     radius=int(rng.integers(0, 4)), window=int(rng.choice([2, 4, 8, 16])), rho=rho,
+                                     lr_mode=int(rng.integers(0, 2)))
+    return out
+
+
+EXTRA.update(_random_cases())
+RANDOM = [k for k in EXTRA if k.startswith("random")]
 NAMES = ["tiny", "tiny_masked", "small_ragged", "small_ragged_corr", "tiny_masked_corr", "ragged_corr_f32", "1k",
          "2k", "4k", "4k_corr", "4k_r2", "ragged"] + list(EXTRA)
 
@@ -36,10 +67,11 @@ def _case(name):
         return U.desc_of(w, host_only=True), O.geometry_of(w)
     a = dict(EXTRA[name])
     lr_mode = a.pop("lr_mode", 0)
+    window, rho = a.get("window", 16), a.get("rho", 4)
     desc = U.make_desc(a["hr_h"], a["hr_w"], a["lr_h"], a["lr_w"], a["n_text"], heads=2, head_dim=128,
-                       dtype="bf16", radius=a["radius"], host_only=True, lr_mode=lr_mode)
-    geo = O.geometry(a["hr_h"], a["hr_w"], a["n_text"], radius=a["radius"], lr_h=a["lr_h"], lr_w=a["lr_w"],
-                     lr_mode=lr_mode)
+                       dtype="bf16", window=window, radius=a["radius"], rho=rho, host_only=True, lr_mode=lr_mode)
+    geo = O.geometry(a["hr_h"], a["hr_w"], a["n_text"], window=window, radius=a["radius"], rho=rho, lr_h=a["lr_h"],
+                     lr_w=a["lr_w"], lr_mode=lr_mode)
     return desc, geo
 
 
