@@ -238,6 +238,26 @@ def test_layer_backward_edge_cases(U, case):
                 grad_close(got[b][:, h], ref, w, f"{case} {n} b{b} h{h}")
 
 
+def _random_bf16():
+    from tests.test_gpu_parity import RANDOM
+    return {k: w for k, w in RANDOM.items() if w.dtype == "bf16"}
+
+
+@pytest.mark.parametrize("name", list(_random_bf16()))
+def test_layer_backward_random_geometries(U, name):
+    """The training layer's backward on the seeded random small bf16
+    geometries of the forward parity tests: dq, dk, dv of every row of every
+    head and image against the oracle."""
+    w = _random_bf16()[name]
+    _, (_, dq, dk, dv) = run_layer_bwd(U, w)
+    for b in range(w.batch):
+        for h, geo, (qh, kh, vh, doh) in oracle_heads(w, range(w.heads), b):
+            rq, rk, rv = O.backward_head(geo, qh, kh, vh, doh, w.rope_theta)
+            grad_close(dq[b][:, h], rq, w, f"{name} dq b{b} h{h}")
+            grad_close(dk[b][:, h], rk, w, f"{name} dk b{b} h{h}")
+            grad_close(dv[b][:, h], rv, w, f"{name} dv b{b} h{h}")
+
+
 def test_backward_is_deterministic(U):
     import torch
     w = WL.WORKLOADS["1k"]

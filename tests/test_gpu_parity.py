@@ -391,6 +391,47 @@ def test_edge_cases(U, case, dtype):
             assert_close(seg_errors(got[:, h], ref, w), tol_of(w), f"{case} {dtype} b{b} h{h}")
 
 
+def _random_workloads(n=32):
+    """Seeded small geometries in the range the edge cases cover (windows of
+    8 and 16, radius 0 to 2), with random grid sizes, text rows, LR grids
+    (default, explicit or none), LR mode, batch, dtype and head_dim."""
+    rng = np.random.default_rng([2026, 78])
+    out = {}
+    for i in range(n):
+        H, W = int(rng.integers(8, 73)), int(rng.integers(8, 73))
+        kind = int(rng.integers(0, 3))
+        lh = -(-H // 4) if kind == 0 else 0 if kind == 1 else int(rng.integers(1, -(-H // 4) + 3))
+        lw = -(-W // 4) if kind == 0 else 0 if kind == 1 else int(rng.integers(1, -(-W // 4) + 3))
+        dtype = "bf16" if i % 3 else "f32"
+        out[f"random{i:02d}"] = WL.Workload(
+            f"random{i:02d}", 200 + i, H, W, lh, lw, int(rng.choice([0, 1, 9, 40])), int(rng.integers(1, 4)),
+            int(rng.choice([64, 128])), dtype, window=int(rng.choice([8, 16])), radius=int(rng.integers(0, 3)),
+            batch=int(rng.integers(1, 3)), lr_mode=int(rng.integers(0, 2)))
+    return out
+
+
+RANDOM = _random_workloads()
+
+
+@pytest.mark.parametrize("name", list(RANDOM))
+def test_random_geometries(U, name):
+    """The layer (fused or not, alternately) on seeded random small
+    geometries: every row of every head and image against the oracle."""
+    import torch
+    w = RANDOM[name]
+    p = plan_of(U, w)
+    q, k, v = qkv_device(w)
+    out = torch.full_like(q, float("nan"))
+    U.Layer(p, fused=int(name[-2:]) % 2 == 0)(q, k, v, out)
+    torch.cuda.synchronize()
+    geo = O.geometry_of(w)
+    for b in range(w.batch):
+        got = to_host_f64(out[b], w.dtype)
+        for h in range(w.heads):
+            ref = O.forward_head(geo, *(WL.head_f64(w, t, h, b) for t in (WL.Q, WL.K, WL.V)), w.rope_theta)
+            assert_close(seg_errors(got[:, h], ref, w), tol_of(w), f"{name} {w} b{b} h{h}")
+
+
 def test_argument_errors_on_device(U):
     import torch
     w = WL.WORKLOADS["tiny"]
