@@ -39,9 +39,10 @@ def U():
     U.use_library(U.LIB_PATH)
 
 
-def _forward(U, w):
-    """The fused and the unfused forward path, and (bf16) the training layer's
-    forward with LSE and its backward; returns every output as host storage."""
+def _forward(U, w, train=None):
+    """The fused and the unfused forward path, and (bf16 workloads of
+    BACKWARD, or train=True) the training layer's forward with LSE and its
+    backward; returns every output as host storage."""
     import torch
     plan = U.ug_plan(U.desc_of(w))
     q, k, v = qkv_device(w)
@@ -50,7 +51,7 @@ def _forward(U, w):
     qp, kp, vp = U.ug_permute(plan, q), U.ug_permute(plan, k), U.ug_permute(plan, v)
     U.ug_rope2d(plan, qp, kp)
     outs["unfused"] = U.ug_unpermute(plan, U.ug_attn_fwd(plan, qp, kp, vp))
-    if w.dtype == "bf16" and w.name in BACKWARD:
+    if w.dtype == "bf16" and (w.name in BACKWARD if train is None else train):
         d_o = to_device(WL.tensor_storage(w, WL.DO), w.dtype)
         train = U.TrainLayer(plan, q.device)
         o = torch.empty_like(q)
@@ -110,6 +111,19 @@ def test_debug_build_warm_start(U, case):
         return {"x_hr": to_host_storage(out, w.dtype)}
 
     _compare(*_both(U, run))
+
+
+def _random8():
+    from tests.test_gpu_parity import RANDOM
+    return dict(list(RANDOM.items())[:8])
+
+
+@pytest.mark.parametrize("name", list(_random8()))
+def test_debug_build_random_geometries(U, name):
+    """Eight of the seeded random geometries of the parity tests, forward
+    and (bf16) backward, through both builds."""
+    w = _random8()[name]
+    _compare(*_both(U, lambda: _forward(U, w, train=True)))
 
 
 def test_debug_words_record_nothing_on_the_release_build(U):
