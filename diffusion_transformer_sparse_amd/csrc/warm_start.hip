@@ -185,6 +185,60 @@ __global__ __launch_bounds__(kWarmThreads) void warm_start_kernel(const T* __res
       }
     }
   };
+  // Output row k of the tile from the column passes of its three LR rows.
+  auto emit_row = [&](int k, const RowWeights& ay, const float (&c0)[E], const float (&c1)[E], const float (&c2)[E],
+                      const float (&b0)[E], const float (&b1)[E], const float (&b2)[E]) {
+    float nf[E];
+    load_f32<T>(reinterpret_cast<const T*>(&nz[k]), nf);
+    float o32[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float acc = ay.ca[0] * c0[e];
+      acc = fmaf(ay.ca[1], c1[e], acc);
+      acc = fmaf(ay.ca[2], c2[e], acc);
+      acc = fmaf(-ay.cb[0], b0[e], acc);
+      acc = fmaf(-ay.cb[1], b1[e], acc);
+      acc = fmaf(-ay.cb[2], b2[e], acc);
+      o32[e] = fmaf(alpha, nf[e], acc);  // acc carries the factor 1 - alpha
+    }
+    u32x4 out;
+    if constexpr (std::is_same<T, float>::value) {
+      float* o = reinterpret_cast<float*>(&out);
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = o32[e];
+    } else {
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = __bf16(o32[e]);
+      out = *reinterpret_cast<u32x4*>(&o);
+    }
+    UG_CHECK(!(col_ok && r0 + k < H) || (g0 + k * row_step >= 0 && g0 + k * row_step < int64_t(H) * W * vpp), 5);
+    if (col_ok && r0 + k < H) __builtin_nontemporal_store(out, outv + g0 + k * row_step);
+  };
+  // Interior tiles at rho 4: the rows' LR bases are b-1 (row 0), b (rows 1-4)
+  // and b+1 (rows 5-7) with b = r0 / 4, so the three sets of column passes
+  // rotate at compile time (row b+2's pass overwrites row b-1's set after
+  // row 0, row b+3's overwrites row b's after row 4) instead of sliding down
+  // with moves as in the general path below.
+  const bool fixed4 = rho == 4 && r0 >= kTileH && r0 + kTileH <= H && (r0 + kTileH - 2) / 4 <= h - 1;
+  if (fixed4) {  // uniform
+    const int32_t b4 = r0 / 4;
+    float c0[E], c1[E], c2[E], d0[E], d1[E], d2[E];
+    column_pass(b4 - 1, c0, d0);
+    column_pass(b4, c1, d1);
+    column_pass(b4 + 1, c2, d2);
+#pragma unroll
+    for (int k = 0; k < kTileH; ++k) {
+      const RowWeights ay = s_ay[k];
+      if (k == 1) column_pass(b4 + 2, c0, d0);
+      if (k == 5) column_pass(b4 + 3, c1, d1);
+      UG_CHECK(ay.base == b4 - 1 + (k == 0 ? 0 : k <= 4 ? 1 : 2), 5);
+      if (k == 0) emit_row(k, ay, c0, c1, c2, d0, d1, d2);
+      else if (k <= 4) emit_row(k, ay, c1, c2, c0, d1, d2, d0);
+      else emit_row(k, ay, c2, c0, c1, d2, d0, d1);
+    }
+    return;
+  }
   float hc[3][E], hb[3][E];
   int32_t held = s_ay[0].base;  // LR row of hc[0] / hb[0] (uniform)
 #pragma unroll
@@ -202,32 +256,7 @@ __global__ __launch_bounds__(kWarmThreads) void warm_start_kernel(const T* __res
       ++held;
       column_pass(held + 2, hc[2], hb[2]);
     }
-    float nf[E];
-    load_f32<T>(reinterpret_cast<const T*>(&nz[k]), nf);
-    float o32[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float acc = ay.ca[0] * hc[0][e];
-      acc = fmaf(ay.ca[1], hc[1][e], acc);
-      acc = fmaf(ay.ca[2], hc[2][e], acc);
-      acc = fmaf(-ay.cb[0], hb[0][e], acc);
-      acc = fmaf(-ay.cb[1], hb[1][e], acc);
-      acc = fmaf(-ay.cb[2], hb[2][e], acc);
-      o32[e] = fmaf(alpha, nf[e], acc);  // acc carries the factor 1 - alpha
-    }
-    u32x4 out;
-    if constexpr (std::is_same<T, float>::value) {
-      float* o = reinterpret_cast<float*>(&out);
-#pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = o32[e];
-    } else {
-      bf16x8 o;
-#pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = __bf16(o32[e]);
-      out = *reinterpret_cast<u32x4*>(&o);
-    }
-    UG_CHECK(!(col_ok && r0 + k < H) || (g0 + k * row_step >= 0 && g0 + k * row_step < int64_t(H) * W * vpp), 5);
-    if (col_ok && r0 + k < H) __builtin_nontemporal_store(out, outv + g0 + k * row_step);
+    emit_row(k, ay, hc[0], hc[1], hc[2], hb[0], hb[1], hb[2]);
   }
 }
 
