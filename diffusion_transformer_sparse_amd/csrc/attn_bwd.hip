@@ -193,32 +193,37 @@ __device__ __forceinline__ void store_block(const f32x16 (&acc)[D / 32], float s
 // ---------------------------------------------------------------------------
 // prep: lse2[bh][row] = lse * log2(e) and delta[bh][row] = sum_d dO * O, in
 // fp32, for rows < L; rows L .. stat_rows-1 are written as zeros.  A
-// workgroup takes kPrepRows rows of up to kPrepHeads heads (grid z covers the
+// workgroup takes kRows rows of up to kPrepHeads heads (grid z covers the
 // head groups): each thread owns one 16-byte column chunk and has four rows
 // of O and dO in flight at once; the D/8 chunks of one head are consecutive
 // lanes and are summed with shuffles.  The sums are collected in LDS, so each
-// head's statistics leave as one contiguous run of kPrepRows floats.
+// head's statistics leave as one contiguous run of kRows floats.  A
+// workgroup walks its rows four at a time, one memory latency each, so small
+// layers (fewer than two 64-row workgroups per compute unit) take 16-row
+// workgroups: four times as many, each a quarter as long.
 // ---------------------------------------------------------------------------
-constexpr int kPrepRows = 64;
+constexpr int kPrepRows = 64;       // rows per workgroup
+constexpr int kPrepRowsSmall = 16;  // rows per workgroup of small layers
 constexpr int kPrepHeads = 64;
 constexpr int kPrepInFlight = 4;
 
-template <int D>
+template <int D, int kRows>
 __global__ __launch_bounds__(1024) void bwd_prep_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ d_o,
                                                         const float* __restrict__ lse, float* __restrict__ lse2,
                                                         float* __restrict__ delta, int32_t L, int32_t Lp,
                                                         int32_t heads) {
+  static_assert(kRows % kPrepInFlight == 0, "rows in whole batches");
   constexpr int C = D / 8;  // chunks per head
-  __shared__ float s_sum[kPrepHeads * kPrepRows];  // [head of the group][row]
+  __shared__ float s_sum[kPrepHeads * kRows];  // [head of the group][row]
   const int32_t h0 = blockIdx.z * kPrepHeads;
   const int32_t gh = min(kPrepHeads, heads - h0);  // heads of this group
   const int32_t units = gh * C;
   const int32_t b = blockIdx.y;
-  const int32_t row0 = blockIdx.x * kPrepRows;
+  const int32_t row0 = blockIdx.x * kRows;
   const int64_t boff = int64_t(b) * L * heads * D + int64_t(h0) * D;
   for (int32_t c0 = 0; c0 < units; c0 += blockDim.x) {  // uniform trip count: every lane shuffles
     const int32_t c = c0 + int32_t(threadIdx.x);
-    for (int32_t rb = 0; rb < kPrepRows; rb += kPrepInFlight) {
+    for (int32_t rb = 0; rb < kRows; rb += kPrepInFlight) {
       bf16x8 x[kPrepInFlight], y[kPrepInFlight];
 #pragma unroll
       for (int r = 0; r < kPrepInFlight; ++r) {
@@ -239,13 +244,13 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(const __bf16* __restrict
         }
 #pragma unroll
         for (int m = C / 2; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, C);
-        if (c < units && c % C == 0) s_sum[(c / C) * kPrepRows + rb + r] = sum;
+        if (c < units && c % C == 0) s_sum[(c / C) * kRows + rb + r] = sum;
       }
     }
   }
   __syncthreads();
-  for (int32_t i = threadIdx.x; i < gh * kPrepRows; i += blockDim.x) {
-    const int32_t h = h0 + i / kPrepRows, row = row0 + i % kPrepRows;
+  for (int32_t i = threadIdx.x; i < gh * kRows; i += blockDim.x) {
+    const int32_t h = h0 + i / kRows, row = row0 + i % kRows;
     if (row >= Lp) continue;
     const int64_t s = (int64_t(b) * heads + h) * Lp + row;
     const bool in = row < L;
@@ -725,10 +730,16 @@ ug_status launch_bwd(ug_plan_t p, BwdParams bp, const __bf16* o, const float* ls
   const int32_t Lp = int32_t(p->stat_rows());
   const int32_t units = std::min(p->d.heads, kPrepHeads) * (D / 8);
   const unsigned prep_threads = unsigned(std::min(1024, (units + 63) / 64 * 64));
-  hipLaunchKernelGGL((bwd_prep_kernel<D>),
-                     dim3(unsigned((Lp + kPrepRows - 1) / kPrepRows), unsigned(p->d.batch),
-                          unsigned((p->d.heads + kPrepHeads - 1) / kPrepHeads)),
-                     dim3(prep_threads), 0, s, o, bp.d_o, lse, lse2, delta, int32_t(p->L), Lp, p->d.heads);
+  const int64_t head_groups = (p->d.heads + kPrepHeads - 1) / kPrepHeads;
+  const bool small = int64_t((Lp + kPrepRows - 1) / kPrepRows) * p->d.batch * head_groups < 2 * int64_t(p->cus);
+  const int rows = small ? kPrepRowsSmall : kPrepRows;
+  const dim3 prep_grid(unsigned((Lp + rows - 1) / rows), unsigned(p->d.batch), unsigned(head_groups));
+  if (small)
+    hipLaunchKernelGGL((bwd_prep_kernel<D, kPrepRowsSmall>), prep_grid, dim3(prep_threads), 0, s, o, bp.d_o, lse, lse2,
+                       delta, int32_t(p->L), Lp, p->d.heads);
+  else
+    hipLaunchKernelGGL((bwd_prep_kernel<D, kPrepRows>), prep_grid, dim3(prep_threads), 0, s, o, bp.d_o, lse, lse2,
+                       delta, int32_t(p->L), Lp, p->d.heads);
   bp.L = int32_t(p->L);
   bp.n_bh = p->d.batch * p->d.heads;
   BwdParams kq = bp;  // the dK/dV pass: the transposed (key-major) tables
