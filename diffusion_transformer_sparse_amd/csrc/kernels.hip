@@ -14,6 +14,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstddef>
 #include <cstdint>
 #include <string>
 #include <type_traits>
@@ -355,6 +356,10 @@ struct AttnParams {
   const ug::Task* tasks;
   const ug::Range* ranges;
   const ug::Block* blocks;
+  // the bf16 kernel's view of blocks[], read with uniform (scalar) loads
+  // (load_item)
+  __attribute__((address_space(4))) const ug::AttnItem* items;
+  int32_t qlen[ug::kXcds];    // items of each XCD queue before its padding
   float scale_log2;      // log2(e) / sqrt(D)
   int32_t T, N;          // text rows, HR rows
   const int32_t* out_perm;     // non-null: write HR output row T+i to raster row T+out_perm[i]
@@ -377,7 +382,9 @@ struct AttnLds {
   static constexpr int kSlots = kTileBytes / 16;      // 16-B slots per tile
   static constexpr int kLoadsPerThread = kSlots / kAttnThreads;
   static_assert(kSlots % kAttnThreads == 0, "tile must split evenly over the workgroup");
-  static constexpr int kTotalBytes = 4 * kTileBytes;  // K ring (2) + V ring (2)
+  // K ring (2 tiles) + V ring (2 tiles); bf16 adds the prologue region
+  // (the next item's K_0 and K_1)
+  static constexpr int kTotalBytes = (kBF ? 6 : 4) * kTileBytes;
   static_assert(kAttnWaves * 32 * D * int(sizeof(T)) <= kTotalBytes, "output staging must fit");
   // physical chunk of logical chunk c in row r
   __device__ static __forceinline__ int k_swz(int r) {  // 16 consecutive rows -> 16 bank groups
@@ -459,6 +466,18 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const char* ktile, const
 
 typedef __attribute__((address_space(4))) const AttnParams* KArgs;
 __device__ __forceinline__ KArgs kernel_args() { return opaque_args<AttnParams>(); }
+
+// Work item `idx`'s record, by uniform loads through the constant address
+// space (scalar loads: the index is wave-uniform).
+__device__ __forceinline__ ug::AttnItem load_item(KArgs kp, int32_t idx) {
+  typedef __attribute__((address_space(4))) const int32_t* CInt;
+  const CInt src = reinterpret_cast<CInt>(kp->items + idx);
+  ug::AttnItem r;
+  int32_t* dst = reinterpret_cast<int32_t*>(&r);
+#pragma unroll
+  for (int k = 0; k < int(sizeof(ug::AttnItem) / 4); ++k) dst[k] = src[k];
+  return r;
+}
 
 // One fp32 query tile (plan item `item`) of the attention.
 template <int D>
@@ -702,11 +721,72 @@ __device__ __forceinline__ void attn_item_f32(KArgs kp, int32_t item, char* smem
 }
 
 
-// One bf16 query tile (plan item `item`) of the attention: the three-stage
-// pipeline described above.
+// The next item's loads, issued before the item starts (at the kernel's
+// start, and in the previous item's epilogue): its first two K tiles into
+// the prologue region (K_0 at 4*TB, K_1 at 5*TB) and its key ranges into
+// s_rng (wave 0, by direct-to-LDS dword loads; rows past the item's ranges
+// read as zeros and are never used) ...
 template <int D>
-__device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* smem, ug::Range* s_rng,
-                                               int32_t* s_item) {
+__device__ __forceinline__ void prefetch_keys(KArgs kp, const ug::AttnItem& it, char* smem, ug::Range* s_rng, int tid,
+                                              int wave, int lane) {
+  using T = __bf16;
+  using Lds = AttnLds<T, D>;
+  constexpr int TB = Lds::kTileBytes;
+  UG_CHECK(it.bh >= 0 && it.bh < kp->n_bh && it.nr >= 1 && it.nr <= ug::kAttnMaxRanges, 0);
+  UG_CHECK(it.ks0 >= 0 && it.nv0 >= 1 && it.nv0 <= kKT && it.ks0 + it.nv0 <= kp->L, 2);
+  UG_CHECK(it.ks1 >= 0 && it.nv1 >= 0 && it.nv1 <= kKT && it.ks1 + it.nv1 <= kp->L, 2);
+  const int32_t b = it.bh / kp->heads, h = it.bh - b * kp->heads;
+  const int64_t rs = kp->row_stride;
+  const T* __restrict__ kg = static_cast<const T*>(kp->k) + int64_t(b) * kp->batch_stride + int64_t(h) * D;
+  TileLoader<T, D, false> kld;
+  kld.init(rs, tid);
+  kld.issue(kg, rs, it.ks0, it.nv0, smem + 4 * TB, tid, wave);
+  kld.issue(kg, rs, it.ks1, it.nv1, smem + 5 * TB, tid, wave);
+  if (wave == 0) {
+    static_assert(ug::kAttnMaxRanges * sizeof(ug::Range) == 2 * 64 * 4, "two dword loads per lane stage the ranges");
+    const char* rbase = reinterpret_cast<const char*>(kp->ranges + it.r0);
+    const int32_t bytes = it.nr * int32_t(sizeof(ug::Range));
+    load_lds<4>(rbase, uint32_t(4 * lane), (lds_void*)s_rng, bytes);
+    load_lds<4>(rbase, uint32_t(256 + 4 * lane), (lds_void*)(reinterpret_cast<char*>(s_rng) + 256), bytes);
+  }
+}
+
+// ... and each wave's 32 query rows into its own 32-row block of the K/V ring
+// area (the block its output is staged in), with the K tiles' chunk swizzle,
+// so the prologue reads the Q operand from LDS.  Rows past the item's end
+// read as zeros (their outputs are never stored).
+template <int D>
+__device__ __forceinline__ void prefetch_queries(KArgs kp, const ug::AttnItem& it, char* smem, int wave, int lane) {
+  using T = __bf16;
+  using Lds = AttnLds<T, D>;
+  constexpr int RB = D * 2;
+  constexpr int kLoads = 32 * RB / 1024;  // 1 KB (64 lanes x 16 B) per load
+  const int32_t b = it.bh / kp->heads, h = it.bh - b * kp->heads;
+  const int64_t rs = kp->row_stride;
+  const int32_t row0 = it.q0 + wave * 32;
+  UG_CHECK(it.q0 >= 0 && it.q0 < it.q1 && it.q1 <= kp->L && it.q1 - it.q0 <= ug::kAttnQueryTile, 1);
+  const T* __restrict__ qg = static_cast<const T*>(kp->q) + int64_t(b) * kp->batch_stride + int64_t(h) * D;
+  const char* base = reinterpret_cast<const char*>(qg + int64_t(min(row0, it.q1)) * rs);
+  const int32_t bytes =
+      __builtin_amdgcn_readfirstlane(min(max(it.q1 - row0, 0), 32) * int32_t(rs) * int32_t(sizeof(T)));
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int slot = i * 64 + lane;
+    const int r = slot / Lds::kChunks;
+    const int lc = (slot % Lds::kChunks) ^ Lds::k_swz(r);
+    load_lds<16>(base, uint32_t(r * rs * int64_t(sizeof(T)) + lc * 16), (lds_void*)(smem + wave * 32 * RB + i * 1024),
+                 bytes);
+  }
+}
+
+// One bf16 query tile (work item `it`) of the attention: the three-stage
+// pipeline described above.  On entry the item's key ranges are in s_rng,
+// its first two K tiles in the prologue region and each wave's queries in
+// its block of the ring area (prefetch_keys, prefetch_queries); the
+// epilogue publishes the next item in s_next_idx and issues its loads.
+template <int D>
+__device__ __forceinline__ void attn_item_bf16(KArgs kp, const ug::AttnItem& it, char* smem, ug::Range* s_rng,
+                                               int32_t* s_next_idx) {
   using T = __bf16;
   using Lds = AttnLds<T, D>;
   constexpr int TB = Lds::kTileBytes;
@@ -719,14 +799,11 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
   constexpr float kHeadroom = 8.0f;         // octaves between the reference and the largest weight seen
   static_assert(kSlots * kExpPerSlot == 32, "32 weights per lane and tile");
 
-  UG_CHECK(item >= 0 && item < kp->queue_len * ug::kXcds, 0);
-  const ug::Block blk = kp->blocks[item];
-  UG_CHECK(blk.task >= 0 && blk.task < kp->n_tasks && blk.bh >= 0 && blk.bh < kp->n_bh, 0);
-  const ug::Task task = kp->tasks[blk.task];
-  UG_CHECK(task.q0 >= 0 && task.q0 < task.q1 && task.q1 <= kp->L && task.q1 - task.q0 <= ug::kAttnQueryTile, 1);
-  const int32_t b = blk.bh / kp->heads, h = blk.bh - b * kp->heads;
+  UG_CHECK(it.bh >= 0 && it.bh < kp->n_bh, 0);
+  UG_CHECK(it.q0 >= 0 && it.q0 < it.q1 && it.q1 <= kp->L && it.q1 - it.q0 <= ug::kAttnQueryTile, 1);
+  UG_CHECK(it.nr >= 1 && it.nr <= ug::kAttnMaxRanges && it.ntiles >= 1, 1);
+  const int32_t b = it.bh / kp->heads, h = it.bh - b * kp->heads;
   const int64_t hoff = int64_t(b) * kp->batch_stride + int64_t(h) * D;
-  const T* __restrict__ qg = static_cast<const T*>(kp->q) + hoff;
   const T* __restrict__ kg = static_cast<const T*>(kp->k) + hoff;
   const T* __restrict__ vg = static_cast<const T*>(kp->v) + hoff;
   T* __restrict__ og = static_cast<T*>(kp->o) + hoff;
@@ -737,34 +814,10 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
   // masked so that alias analysis keeps its range
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (kAttnWaves - 1);
   const int l32 = lane & 31, g = lane >> 5;
-  const int32_t qrow = task.q0 + wave * 32 + l32;
-  const int32_t qload = qrow < task.q1 ? qrow : task.q1 - 1;
+  const int32_t qrow = it.q0 + wave * 32 + l32;
   const float c2 = kp->scale_log2;
-
-  // The task's key ranges (at most ug::kAttnMaxRanges, checked at launch)
-  // are staged in LDS, so moving to the next range inside the tile loop is an
-  // LDS read rather than a global load that would wait on the tile loads in
-  // flight.
-  const int32_t nr = task.r1 - task.r0;
-  UG_CHECK(nr >= 1 && nr <= ug::kAttnMaxRanges, 1);
-  if (tid < nr) {
-    const ug::Range r = kp->ranges[task.r0 + tid];
-    UG_CHECK(r.k0 >= 0 && r.k0 < r.k1 && r.k1 <= kp->L, 1);
-    s_rng[tid] = r;
-  }
-
-  // The wave's queries as the B operand of S^T = K Q^T.
-  bf16x8 qf[kQRegs];
-#pragma unroll
-  for (int i = 0; i < kQRegs; ++i) qf[i] = *reinterpret_cast<const bf16x8*>(qg + qload * rs + 16 * i + 8 * g);
-  __syncthreads();  // s_rng is filled
-
-  int32_t ntiles = 0;
-  for (int32_t r = 0; r < nr; ++r) {
-    const ug::Range rg = s_rng[r];
-    ntiles += (rg.k1 - rg.k0 + kKT - 1) / kKT;
-  }
-  ntiles = __builtin_amdgcn_readfirstlane(ntiles);  // uniform: it feeds scalar buffer descriptors
+  const int32_t nr = it.nr;
+  const int32_t ntiles = it.ntiles;
 
   // Per-lane LDS byte offsets.  K operand of k-step i: row l32 (plus 32 per
   // block), logical chunk of dims 16i + 8g.
@@ -785,15 +838,24 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
     voff[t] = vrow * RB + (((dim / 8) ^ Lds::v_swz(vrow)) * 16) + (dim % 8) * 2;
   }
 
+  // The wave's queries as the B operand of S^T = K Q^T, from the wave's
+  // block of the ring area (same row and chunk layout as a K tile).
+  bf16x8 qf[kQRegs];
+#pragma unroll
+  for (int i = 0; i < kQRegs; ++i) qf[i] = *reinterpret_cast<const bf16x8*>(smem + wave * 32 * RB + koff[i]);
+
   f32x16 acc[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
   float mref;        // softmax reference, log2 units of the scaled logits
   float lsum = 0.f;  // this lane half's share of the row sum
 
+  // K_0 and K_1 are already loaded, so the K cursor starts at tile 2.
   TileCursor ck, cv;  // next K tile to load, next V tile to load
   ck.init(s_rng, 0, nr);
   cv = ck;
+  ck.advance(s_rng);
+  ck.advance(s_rng);
   TileLoader<T, D, false> kld;
   TileLoader<T, D, true> vld;
   kld.init(rs, tid);
@@ -904,25 +966,16 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
     }
   };
 
-  // prologue: K_0 -> K slot 0, K_1 -> K slot 1; S_0; the reference is
-  // kHeadroom above tile 0's maximum
-  const int32_t nv0 = ck.nv();
-  kld.issue(kg, rs, ck.ks, nv0, smem, tid, wave);
-  ck.advance(s_rng);
-  int32_t nv_pend = kKT;  // rows of the K tile issued most recently (tile i+1 at the start of step i)
-  if (ntiles > 1) {
-    nv_pend = ck.nv();
-    kld.issue(kg, rs, ck.ks, nv_pend, smem + TB, tid, wave);
-    ck.advance(s_rng);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // prologue: S_0 from K_0 (prologue region); the reference is kHeadroom
+  // above tile 0's maximum
+  const int32_t nv0 = it.nv0;
+  int32_t nv_pend = ntiles > 1 ? it.nv1 : kKT;  // rows of the K tile issued most recently (tile i+1 at step i)
   f32x16 sa[2], sb[2];
   bf16x8 pa[4], pb[4];
-  qk_tile<T, D>(sa, smem, qf, koff);
+  qk_tile<T, D>(sa, smem + 4 * TB, qf, koff);
   if (nv0 < kKT) mask_tail(sa, nv0);
   mref = tile_max(sa) * c2 + kHeadroom;
-  __syncthreads();  // step 0 overwrites K slot 0 with K_2
+  __syncthreads();  // step 0's loads overwrite the Q rows of waves 0, 1, 4 and 5 (K slot 0, V slot 0)
 
   // Loads of step i: K_{i+2} -> K slot i&1 (K_i was read in step i-1),
   // V_i -> V slot i&1 (V_{i-2} was read in step i-1).
@@ -947,7 +1000,7 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
     float d = 0.f;
     weights_all(sa, pa, d);
     if (ntiles > 1) {
-      qk_tile<T, D>(sb, smem + TB, qf, koff);
+      qk_tile<T, D>(sb, smem + 5 * TB, qf, koff);
       if (nv_s < kKT) mask_tail(sb, nv_s);
     }
     lsum += d;
@@ -955,6 +1008,13 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
     __syncthreads();
   }
 
+  // Step i in [1, ntiles): QK^T(i+1) || weights(i) || PV(i-1) as 2*(D/8)
+  // slots of one MFMA each (even: QK^T, odd: PV), the operand reads kLead
+  // slots ahead and 32/slots weights of tile i per slot.  The slots are
+  // fenced, so the compiler keeps this interleave.  The last step
+  // (i = ntiles - 1, `last`) has no tile i+1: its even slots hold weights
+  // only, it loads no K tile, and one thread takes the cursor of the next
+  // item, so that its atomic is in flight during the step.
   // Step i in [1, ntiles): QK^T(i+1) || weights(i) || PV(i-1) as 2*(D/8)
   // slots of one MFMA each (even: QK^T, odd: PV), the operand reads kLead
   // slots ahead and 32/slots weights of tile i per slot.  The slots are
@@ -1038,32 +1098,35 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
   // Pairs of steps, so that the ring slots and register sets are fixed at
   // compile time; the loop has no exit between the two (an exit there keeps
   // both weight sets alive across the pair and spills).
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   int32_t i = 1;
   for (; i + 1 < ntiles; i += 2) {
-    step(i, std::integral_constant<int, 1>{}, sb, sa, pa, pb);
-    step(i + 1, std::integral_constant<int, 0>{}, sa, sb, pb, pa);
+    step(i, P1{}, sb, sa, pa, pb);
+    step(i + 1, P0{}, sa, sb, pb, pa);
   }
   if (i < ntiles)  // one odd step left; the weights of the last tile land in pb, its V in slot 1
-    step(i, std::integral_constant<int, 1>{}, sb, sa, pa, pb);
+    step(i, P1{}, sb, sa, pa, pb);
 
   // ---- epilogue: combine the lane halves' row sums, normalise, and write
   // the wave's 32 x D output block through LDS (swizzled rows) as full rows.
-  // The next item's cursor is taken first, so that its atomic is in flight
-  // during the epilogue, and the output rows' destinations are looked up
-  // before the last PV.
+  // Thread 0 takes the own queue's cursor for the next item first, and the
+  // destination rows are looked up (branch-free table reads, all in flight
+  // together; rows past the tile are clamped for the lookup and skipped at
+  // the store) before the last PV.  The next item is published at the
+  // barrier that frees the LDS; its record is read while the output is
+  // staged, and its loads go out after the output stores.
   kp = kernel_args();  // the epilogue's arguments are loaded here, not kept across the loop
   const int32_t x0 = xcc_id();
   int32_t cnext = 0;
   if (tid == 0) cnext = __hip_atomic_fetch_add(kp->queue + x0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   constexpr int rows_per_pass = 64 / Lds::kChunks;
   constexpr int kPasses = 32 / rows_per_pass;
-  // Destination rows as branch-free table reads (rows past the tile are
-  // clamped for the lookup and skipped at the store), all in flight together.
   int32_t orow[kPasses];
   if (kp->out_perm) {  // uniform
 #pragma unroll
     for (int pass = 0; pass < kPasses; ++pass) {
-      const int32_t row = min(task.q0 + wave * 32 + pass * rows_per_pass + lane / Lds::kChunks, task.q1 - 1);
+      const int32_t row = min(it.q0 + wave * 32 + pass * rows_per_pass + lane / Lds::kChunks, it.q1 - 1);
       const bool hr = row >= kp->T && row < kp->T + kp->N;
       const bool lr = row >= kp->T + kp->N && kp->out_lr_perm != nullptr;
       const int32_t* tab = lr ? kp->out_lr_perm : kp->out_perm;
@@ -1074,7 +1137,7 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
   } else {
 #pragma unroll
     for (int pass = 0; pass < kPasses; ++pass)
-      orow[pass] = task.q0 + wave * 32 + pass * rows_per_pass + lane / Lds::kChunks;
+      orow[pass] = it.q0 + wave * 32 + pass * rows_per_pass + lane / Lds::kChunks;
   }
   if ((ntiles - 1) & 1)  // the weights of the last tile are in pb (odd) or pa (even), its V in that slot
     pv_all(pb, smem + 3 * TB);
@@ -1082,10 +1145,21 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
     pv_all(pa, smem + 2 * TB);
   const float total = pair_sum(lsum);
   const float inv = 1.0f / total;
-  UG_CHECK(!(kp->lse && g == 0 && qrow < task.q1) || qrow < kp->lse_rows, 3);
-  if (kp->lse && g == 0 && qrow < task.q1)  // log(sum_j exp(s_j)) = (mref + log2(total)) * ln 2
-    kp->lse[int64_t(blk.bh) * kp->lse_rows + qrow] = (mref + __log2f(total)) * 0.6931471805599453f;
-  __syncthreads();  // every wave has read the last V tile before the staging below overwrites it
+  UG_CHECK(!(kp->lse && g == 0 && qrow < it.q1) || qrow < kp->lse_rows, 3);
+  if (kp->lse && g == 0 && qrow < it.q1)  // log(sum_j exp(s_j)) = (mref + log2(total)) * ln 2
+    kp->lse[int64_t(it.bh) * kp->lse_rows + qrow] = (mref + __log2f(total)) * 0.6931471805599453f;
+  // The next item: the cursor taken above if it lies within the own queue's
+  // items (past them the queue holds padding), else the usual search over
+  // the queues (which moves the own queue's cursor once more, as a failed
+  // grab does).
+  if (tid == 0) {
+    const int32_t next = cnext < kp->qlen[x0] ? cnext * ug::kXcds + x0
+                                              : queue_grab(kp->queue, kp->queue_len, kp->blocks, x0);
+    UG_CHECK(next < kp->queue_len * ug::kXcds, 0);
+    *s_next_idx = next;
+  }
+  __syncthreads();  // every wave has read the last V tile; the next item is published
+  const int32_t next = __builtin_amdgcn_readfirstlane(*s_next_idx);
   char* const ost = smem + wave * 32 * RB;
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
@@ -1098,18 +1172,6 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
       for (int e = 0; e < 4; ++e) w[e] = __bf16(acc[t][4 * q4 + e] * inv);
       *reinterpret_cast<bf16x4*>(dst) = w;
     }
-  // The next item, before the output stores (whose completion a wait on
-  // the cursor's atomic would otherwise include): the cursor taken above if
-  // it names one, else the usual search over the queues (which moves the
-  // own queue's cursor once more, as a failed grab does).
-  if (tid == 0) {
-    int32_t next;
-    if (cnext < kp->queue_len && kp->blocks[cnext * ug::kXcds + x0].task >= 0)
-      next = cnext * ug::kXcds + x0;
-    else
-      next = queue_grab(kp->queue, kp->queue_len, kp->blocks, x0);
-    *s_item = next;
-  }
   // each wave reads back only its own block: LDS operations of one wave
   // complete in order, so no barrier is needed between the write and read.
 #pragma unroll
@@ -1117,10 +1179,19 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, int32_t item, char* sme
     const int r = pass * rows_per_pass + lane / Lds::kChunks;
     const int cc = lane % Lds::kChunks;
     const uint4 val = *reinterpret_cast<const uint4*>(ost + r * RB + ((cc ^ Lds::k_swz(r)) * 16));
-    if (task.q0 + wave * 32 + r < task.q1) {
+    if (it.q0 + wave * 32 + r < it.q1) {
       UG_CHECK(orow[pass] >= 0 && orow[pass] < kp->L, 3);
       *reinterpret_cast<uint4*>(og + int64_t(orow[pass]) * rs + cc * Lds::kEl16) = val;
     }
+  }
+  // The next item's first loads: its K_0, K_1 and ranges into the prologue
+  // region and s_rng, and its queries into the wave's block once the wave's
+  // reads of it have completed.
+  if (next >= 0) {
+    const ug::AttnItem nx = load_item(kp, next);
+    prefetch_keys<D>(kp, nx, smem, s_rng, tid, wave, lane);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    prefetch_queries<D>(kp, nx, smem, wave, lane);
   }
 }
 
@@ -1131,23 +1202,47 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(AttnParams p) {
   using Lds = AttnLds<T, D>;
   __shared__ __attribute__((aligned(1024))) char smem[Lds::kTotalBytes];
   __shared__ ug::Range s_rng[ug::kAttnMaxRanges];
-  __shared__ int32_t s_item;
-  if (threadIdx.x == 0) {
-    KArgs kp = kernel_args();
-    s_item = queue_grab(kp->queue, kp->queue_len, kp->blocks, xcc_id());
-  }
-  __syncthreads();
-  for (;;) {
-    const int32_t item = s_item;
-    if (item < 0) break;
-    if constexpr (std::is_same<T, __bf16>::value) {
-      // the item names the next one in s_item before it returns
-      attn_item_bf16<D>(kernel_args(), item, smem, s_rng, &s_item);
-      // The next item reuses the LDS and reads s_item; the output stores
-      // need not have landed (an LDS-only wait, no memory fence).
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-      __builtin_amdgcn_s_barrier();
-    } else {
+  if constexpr (std::is_same<T, __bf16>::value) {
+    // The next item is published in s_next_idx, and its first loads are
+    // issued, before it starts: here for the first item, in the previous
+    // item's epilogue for the others.
+    __shared__ int32_t s_next_idx;
+    if (threadIdx.x == 0) {
+      KArgs kp = kernel_args();
+      s_next_idx = queue_grab(kp->queue, kp->queue_len, kp->blocks, xcc_id());
+    }
+    __syncthreads();
+    {
+      const int tid = opaque_tid<kAttnThreads>();
+      const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (kAttnWaves - 1);
+      const int32_t first = __builtin_amdgcn_readfirstlane(s_next_idx);
+      if (first >= 0) {
+        KArgs kp = kernel_args();
+        const ug::AttnItem nx = load_item(kp, first);
+        prefetch_keys<D>(kp, nx, smem, s_rng, tid, wave, lane);
+        prefetch_queries<D>(kp, nx, smem, wave, lane);
+      }
+    }
+    for (;;) {
+      __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of the item's ranges, K_0, K_1 and Q have landed
+      __syncthreads();
+      const int32_t idx = __builtin_amdgcn_readfirstlane(s_next_idx);
+      if (idx < 0) break;
+      KArgs kp = kernel_args();
+      UG_CHECK(idx < kp->queue_len * ug::kXcds, 0);
+      const ug::AttnItem it = load_item(kp, idx);
+      attn_item_bf16<D>(kp, it, smem, s_rng, &s_next_idx);
+    }
+  } else {
+    __shared__ int32_t s_item;
+    if (threadIdx.x == 0) {
+      KArgs kp = kernel_args();
+      s_item = queue_grab(kp->queue, kp->queue_len, kp->blocks, xcc_id());
+    }
+    __syncthreads();
+    for (;;) {
+      const int32_t item = s_item;
+      if (item < 0) break;
       attn_item_f32<D>(kernel_args(), item, smem, s_rng);
       __syncthreads();  // the next item reuses the LDS and s_item
       if (threadIdx.x == 0) {
@@ -1225,6 +1320,9 @@ ug_status attn_common(ug_plan_t p, const void* q, const void* k, const void* v, 
   ap.tasks = p->d_tasks;
   ap.ranges = p->d_ranges;
   ap.blocks = p->d_blocks;
+  ap.items = reinterpret_cast<__attribute__((address_space(4))) const ug::AttnItem*>(
+      reinterpret_cast<uintptr_t>(p->d_items));
+  for (int x = 0; x < ug::kXcds; ++x) ap.qlen[x] = p->queue_items[x];
   ap.scale_log2 = float(1.4426950408889634 / std::sqrt(double(p->d.head_dim)));
   ap.T = int32_t(p->T);
   ap.N = int32_t(p->N);

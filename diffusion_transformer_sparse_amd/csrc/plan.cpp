@@ -449,6 +449,35 @@ std::vector<ug::Block> order_blocks(const std::vector<ug::Task>& tasks, const st
   return blocks;
 }
 
+// The forward's item records: each queue item's task fields, tile count
+// and first two 64-key tiles, walked as the kernel walks the key ranges
+// (range after range, a range's last tile holding its remaining rows).
+std::vector<ug::AttnItem> attn_items(const std::vector<ug::Block>& blocks, const std::vector<ug::Task>& tasks,
+                                     const std::vector<ug::Range>& ranges) {
+  std::vector<ug::AttnItem> items(blocks.size(), ug::AttnItem{0, 0, 0, 0, -1, 0, 0, 0, 0, 0, 0, 0});
+  for (size_t k = 0; k < blocks.size(); ++k) {
+    if (blocks[k].task < 0) continue;
+    const ug::Task& t = tasks[blocks[k].task];
+    ug::AttnItem& it = items[k];
+    it.q0 = t.q0;
+    it.q1 = t.q1;
+    it.r0 = t.r0;
+    it.nr = t.r1 - t.r0;
+    it.bh = blocks[k].bh;
+    it.ntiles = int32_t(tiles_of(ranges, t));
+    int32_t got = 0;
+    for (int r = t.r0; r < t.r1 && got < 2; ++r)
+      for (int32_t ks = ranges[r].k0; ks < ranges[r].k1 && got < 2; ks += ug::kAttnKeyTile, ++got) {
+        const int32_t nv = std::min(ug::kAttnKeyTile, ranges[r].k1 - ks);
+        (got == 0 ? it.ks0 : it.ks1) = ks;
+        (got == 0 ? it.nv0 : it.nv1) = nv;
+      }
+    if (got < 2) it.ks1 = it.ks0;  // one tile only: the second load reads no rows
+    if (it.nr < 1 || it.ntiles < 1 || it.nv0 < 1) throw std::logic_error("attention item without key tiles");
+  }
+  return items;
+}
+
 // Morton (Z-order) code of a window's (row, column): consecutive codes stay
 // in compact 2D blocks, so the query tiles that run at the same time on one
 // XCD share more of their neighbour windows' K/V tiles in its L2.
@@ -477,6 +506,16 @@ void build_blocks(ug_plan_s& p) {
     }
   }
   p.blocks = order_blocks(p.tasks, p.ranges, BH, locality, true);
+  p.items = attn_items(p.blocks, p.tasks, p.ranges);
+  // Each XCD queue's items come first and its padding after them.
+  const size_t len = p.blocks.size() / ug::kXcds;
+  for (int x = 0; x < ug::kXcds; ++x) {
+    int32_t n = 0;
+    while (size_t(n) < len && p.blocks[size_t(n) * ug::kXcds + x].task >= 0) ++n;
+    for (size_t k = size_t(n); k < len; ++k)
+      if (p.blocks[k * ug::kXcds + x].task >= 0) throw std::logic_error("work-queue item after padding");
+    p.queue_items[x] = n;
+  }
   // The dK/dV pass's long items (key tiles every query sees) stay spread
   // over the XCDs: grouped, 18 of them stream the same rows at once and the
   // pass ran 2.5-3% slower although it fetched less than half as much.
@@ -500,7 +539,7 @@ ug_status upload(const std::vector<T>& h, T** d) {
 
 void free_device(ug_plan_s* p) {
   void* ptrs[] = {p->d_perm,    p->d_inv,     p->d_lr_perm, p->d_lr_inv,     p->d_rope,
-                  p->d_tasks,   p->d_ranges,  p->d_blocks,  p->d_ktasks,     p->d_kranges,
+                  p->d_tasks,   p->d_ranges,  p->d_blocks,  p->d_items,      p->d_ktasks,     p->d_kranges,
                   p->d_kblocks, p->d_kmasks, p->d_kmask_off, p->d_queue};
   for (void* q : ptrs)
     if (q) (void)hipFree(q);
@@ -520,6 +559,7 @@ void free_device(ug_plan_s* p) {
   p->d_tasks = nullptr;
   p->d_ranges = nullptr;
   p->d_blocks = nullptr;
+  p->d_items = nullptr;
   p->d_ktasks = nullptr;
   p->d_kranges = nullptr;
   p->d_kblocks = nullptr;
@@ -633,6 +673,7 @@ ug_status ug_plan(const ug_desc* user_desc, ug_plan_t* out) {
     if (s == UG_OK) s = ug::upload(p->tasks, &p->d_tasks);
     if (s == UG_OK) s = ug::upload(p->ranges, &p->d_ranges);
     if (s == UG_OK) s = ug::upload(p->blocks, &p->d_blocks);
+    if (s == UG_OK) s = ug::upload(p->items, &p->d_items);
     if (s == UG_OK) s = ug::upload(p->ktasks, &p->d_ktasks);
     if (s == UG_OK) s = ug::upload(p->kranges, &p->d_kranges);
     if (s == UG_OK) s = ug::upload(p->kblocks, &p->d_kblocks);

@@ -30,6 +30,14 @@ struct Range {
 struct Block {
   int32_t task, bh;
 };
+// The attention forward's view of one work item (Block): its query rows, its
+// key ranges (ranges[r0 .. r0 + nr)), (batch, head), its 64-key tile count
+// and its first two tiles (start row, rows; a tile that does not exist has
+// 0 rows), so that one record read is enough to start the item's loads.
+// nr == 0 marks an idle item (Block::task < 0).
+struct AttnItem {
+  int32_t q0, q1, r0, nr, bh, ntiles, ks0, nv0, ks1, nv1, pad0, pad1;
+};
 
 constexpr int kAttnQueryTile = 256;  // query rows per workgroup (8 waves x 32)
 constexpr int kAttnKeyTile = 64;     // key rows per LDS stage
@@ -62,6 +70,8 @@ struct ug_plan_s {
   std::vector<ug::Task> tasks;
   std::vector<ug::Range> ranges;
   std::vector<ug::Block> blocks;
+  std::vector<ug::AttnItem> items;  // one per blocks[] entry
+  int32_t queue_items[ug::kXcds] = {};  // items of each XCD queue before its padding
   int64_t pairs = 0;      // allowed (q, k) pairs per (batch, head)
   int64_t key_tiles = 0;  // 64-key tiles per (batch, head)
   int32_t max_nbr = 0;
@@ -95,6 +105,7 @@ struct ug_plan_s {
   ug::Task* d_tasks = nullptr;
   ug::Range* d_ranges = nullptr;
   ug::Block* d_blocks = nullptr;
+  ug::AttnItem* d_items = nullptr;
   ug::Task* d_ktasks = nullptr;
   ug::Range* d_kranges = nullptr;
   ug::Block* d_kblocks = nullptr;
