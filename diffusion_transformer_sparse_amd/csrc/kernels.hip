@@ -1015,18 +1015,55 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, const ug::AttnItem& it,
   // (i = ntiles - 1, `last`) has no tile i+1: its even slots hold weights
   // only, it loads no K tile, and one thread takes the cursor of the next
   // item, so that its atomic is in flight during the step.
-  // Step i in [1, ntiles): QK^T(i+1) || weights(i) || PV(i-1) as 2*(D/8)
+  // The epilogue's first reads.  At the start of the last step (or of the
+  // epilogue, for an item of one tile) thread 0 takes the own queue's cursor
+  // for the next item, so the atomic is in flight during the step; once the
+  // step's loads have landed (the cursor with them) every lane looks up the
+  // permutation entries of its output rows (raster output: branch-free table
+  // reads, rows past the tile clamped for the lookup and skipped at the
+  // store), all in flight during the last PV.  The variables are declared
+  // without values, so nothing of this is live across the tile loop.
+  constexpr int rows_per_pass = 64 / Lds::kChunks;
+  constexpr int kPasses = 32 / rows_per_pass;
+  int32_t cnext;          // thread 0: the own queue's cursor for the next item
+  int32_t oent[kPasses];  // raster output: the permutation entry of each output row
+  auto take_cursor = [&]() {
+    if (tid == 0) {
+      KArgs ka = kernel_args();
+      cnext = __hip_atomic_fetch_add(ka->queue + xcc_id(), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  auto out_row = [&](int pass) {  // the tile row of output pass `pass`, clamped into the tile
+    return min(it.q0 + wave * 32 + pass * rows_per_pass + lane / Lds::kChunks, it.q1 - 1);
+  };
+  auto look_up_rows = [&]() {
+    KArgs ka = kernel_args();
+    const int32_t* perm = ka->out_perm;
+    if (perm) {  // uniform
+      const int32_t* lrp = ka->out_lr_perm;
+      asm volatile("" : "+s"(perm), "+s"(lrp));  // two scalar pointers; the table is picked per lane
+      const int32_t T0 = ka->T, N0 = ka->N;
+#pragma unroll
+      for (int pass = 0; pass < kPasses; ++pass) {
+        const int32_t row = out_row(pass);
+        const bool hr = row >= T0 && row < T0 + N0;
+        const bool lr = row >= T0 + N0 && lrp != nullptr;
+        const int32_t* tab = lr ? lrp : perm;
+        oent[pass] = tab[hr ? row - T0 : lr ? row - T0 - N0 : 0];
+      }
+    }
+  };
+
+  // Step i in [1, ntiles - 1): QK^T(i+1) || weights(i) || PV(i-1) as 2*(D/8)
   // slots of one MFMA each (even: QK^T, odd: PV), the operand reads kLead
   // slots ahead and 32/slots weights of tile i per slot.  The slots are
-  // fenced, so the compiler keeps this interleave.  QK^T of tile ntiles (past
-  // the end, from a stale K slot) is computed and never used.
+  // fenced, so the compiler keeps this interleave.
   auto step = [&](int32_t i, auto par, f32x16(&s_cur)[2], f32x16(&s_nxt)[2], bf16x8(&p_cur)[4],
                   bf16x8(&p_nxt)[4]) {
     constexpr int PAR = decltype(par)::value;                   // i & 1
     const char* const k_next = smem + (PAR ? 0 : TB);           // K_{i+1}
     const char* const v_prev = smem + 2 * TB + (PAR ? 0 : TB);  // V_{i-1}
     const int32_t nv_s = nv_pend;                               // rows of tile i+1
-    const bool has_s = i + 1 < ntiles;
     // The step's loads (K_{i+2} and V_i, as issue_loads) go out one at a time,
     // kLoadGap slots apart, rather than all at the step's start, where the
     // eight waves' loads and their first operand reads would meet.  With no
@@ -1088,10 +1125,56 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, const ug::AttnItem& it,
       __builtin_amdgcn_sched_barrier(0);
     }
     sum_last(d);
-    if (has_s && nv_s < kKT) mask_tail(s_nxt, nv_s);  // uniform (scalar) condition
+    if (nv_s < kKT) mask_tail(s_nxt, nv_s);  // uniform (scalar) condition
     if (__ballot(!(d < 256.0f))) settle(s_cur, p_nxt, d);
     lsum += d;
     __builtin_amdgcn_s_waitcnt(0);  // this thread's direct-to-LDS loads have landed
+    __syncthreads();
+  };
+
+  // The last step (i = ntiles - 1): weights(i) || PV(i-1), with no tile i+1
+  // and so no QK^T and no K load; the odd slots hold the PV MFMAs, every slot
+  // its weights.  Its ring slots follow i's parity at run time (one form for
+  // both parities): V_{i-1} is read from slot (i-1)&1 and V_i goes to slot i&1.
+  auto last_step = [&](int32_t i, f32x16(&s_cur)[2], bf16x8(&p_cur)[4], bf16x8(&p_nxt)[4]) {
+    take_cursor();
+    const int32_t vpar = (i & 1) * TB;
+    const char* const v_prev = smem + 3 * TB - vpar;  // V_{i-1}
+    char* const v_dst = smem + 2 * TB + vpar;          // V_i
+    const char* const vbase = reinterpret_cast<const char*>(vg + int64_t(cv.ks) * rs);
+    const int32_t vbytes = __builtin_amdgcn_readfirstlane(cv.nv() * int32_t(rs) * int32_t(sizeof(T)));
+    constexpr int kLPT = Lds::kLoadsPerThread;
+    constexpr int kLoadGap = D == 64 ? 4 : 2;
+    bf16x8 opnd[kLead + 1];
+    auto fetch = [&](int k) {  // odd slots only
+      const int j = k >> 1;
+      const char* a0 = v_prev + voff[j % (D / 32)] + (16 * (j / (D / 32))) * RB;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * RB));
+      opnd[k % (kLead + 1)] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+#pragma unroll
+    for (int k = 1; k < kLead; k += 2) fetch(k);
+    float d = 0.f;
+#pragma unroll
+    for (int k = 0; k < kSlots; ++k) {
+      if (k % kLoadGap == 0 && k / kLoadGap < 2 * kLPT && (k / kLoadGap) % 2 == 1)
+        vld.issue_one((k / kLoadGap) >> 1, vbase, vbytes, v_dst, wave);
+      if (k + kLead < kSlots && ((k + kLead) & 1)) fetch(k + kLead);
+      if (k & 1) {
+        const int j = k >> 1;
+        acc[j % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[k % (kLead + 1)], p_cur[j / (D / 32)],
+                                                                    acc[j % (D / 32)], 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < kExpPerSlot; ++e) weight(s_cur, p_nxt, d, k * kExpPerSlot + e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    sum_last(d);
+    if (__ballot(!(d < 256.0f))) settle(s_cur, p_nxt, d);
+    lsum += d;
+    __builtin_amdgcn_s_waitcnt(0);  // V_i, and the cursor, have landed
+    look_up_rows();
     __syncthreads();
   };
 
@@ -1100,55 +1183,56 @@ __device__ __forceinline__ void attn_item_bf16(KArgs kp, const ug::AttnItem& it,
   // both weight sets alive across the pair and spills).
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
+  // The pairs stop before the last step, which then runs in the even
+  // form's registers: scores of the last tile in sa, weights of the tile
+  // before it in pb; the last tile's weights land in pa.
   int32_t i = 1;
-  for (; i + 1 < ntiles; i += 2) {
+  for (; i + 2 < ntiles; i += 2) {
     step(i, P1{}, sb, sa, pa, pb);
     step(i + 1, P0{}, sa, sb, pb, pa);
   }
-  if (i < ntiles)  // one odd step left; the weights of the last tile land in pb, its V in slot 1
-    step(i, P1{}, sb, sa, pa, pb);
+  if (i < ntiles) {
+    if (i + 1 < ntiles) {  // two steps left: the odd one, then the last
+      step(i, P1{}, sb, sa, pa, pb);
+      ++i;
+    } else {  // the last step is odd: its operands move to the even form's registers
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) sa[mb] = sb[mb];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) pb[c] = pa[c];
+    }
+    last_step(i, sa, pb, pa);
+  } else {  // one tile: its weights (step 0) are in pa, its V in slot 0
+    take_cursor();
+    look_up_rows();
+  }
 
-  // ---- epilogue: combine the lane halves' row sums, normalise, and write
-  // the wave's 32 x D output block through LDS (swizzled rows) as full rows.
-  // Thread 0 takes the own queue's cursor for the next item first, and the
-  // destination rows are looked up (branch-free table reads, all in flight
-  // together; rows past the tile are clamped for the lookup and skipped at
-  // the store) before the last PV.  The next item is published at the
+  // ---- epilogue: the last PV; combine the lane halves' row sums,
+  // normalise, and write the wave's 32 x D output block through LDS
+  // (swizzled rows) as full rows.  The next item is published at the
   // barrier that frees the LDS; its record is read while the output is
   // staged, and its loads go out after the output stores.
   kp = kernel_args();  // the epilogue's arguments are loaded here, not kept across the loop
   const int32_t x0 = xcc_id();
-  int32_t cnext = 0;
-  if (tid == 0) cnext = __hip_atomic_fetch_add(kp->queue + x0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  constexpr int rows_per_pass = 64 / Lds::kChunks;
-  constexpr int kPasses = 32 / rows_per_pass;
+  pv_all(pa, smem + 2 * TB + ((ntiles - 1) & 1) * TB);  // the last tile's weights, its V in slot (ntiles-1)&1
   int32_t orow[kPasses];
-  if (kp->out_perm) {  // uniform
 #pragma unroll
-    for (int pass = 0; pass < kPasses; ++pass) {
-      const int32_t row = min(it.q0 + wave * 32 + pass * rows_per_pass + lane / Lds::kChunks, it.q1 - 1);
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int32_t row = out_row(pass);
+    if (kp->out_perm) {  // uniform
       const bool hr = row >= kp->T && row < kp->T + kp->N;
       const bool lr = row >= kp->T + kp->N && kp->out_lr_perm != nullptr;
-      const int32_t* tab = lr ? kp->out_lr_perm : kp->out_perm;
-      const int32_t idx = hr ? row - kp->T : lr ? row - kp->T - kp->N : 0;
-      const int32_t v = tab[idx];
-      orow[pass] = hr ? kp->T + v : lr ? kp->T + kp->N + v : row;
+      orow[pass] = hr ? kp->T + oent[pass] : lr ? kp->T + kp->N + oent[pass] : row;
+    } else {
+      orow[pass] = row;
     }
-  } else {
-#pragma unroll
-    for (int pass = 0; pass < kPasses; ++pass)
-      orow[pass] = it.q0 + wave * 32 + pass * rows_per_pass + lane / Lds::kChunks;
   }
-  if ((ntiles - 1) & 1)  // the weights of the last tile are in pb (odd) or pa (even), its V in that slot
-    pv_all(pb, smem + 3 * TB);
-  else
-    pv_all(pa, smem + 2 * TB);
   const float total = pair_sum(lsum);
   const float inv = 1.0f / total;
   UG_CHECK(!(kp->lse && g == 0 && qrow < it.q1) || qrow < kp->lse_rows, 3);
   if (kp->lse && g == 0 && qrow < it.q1)  // log(sum_j exp(s_j)) = (mref + log2(total)) * ln 2
     kp->lse[int64_t(it.bh) * kp->lse_rows + qrow] = (mref + __log2f(total)) * 0.6931471805599453f;
-  // The next item: the cursor taken above if it lies within the own queue's
+  // The next item: the cursor taken in the last step if it lies within the own queue's
   // items (past them the queue holds padding), else the usual search over
   // the queues (which moves the own queue's cursor once more, as a failed
   // grab does).
